@@ -1,0 +1,573 @@
+"""Pins for the float64 oracle against what the rl-triton pages and mathematics fix.
+
+Each check compares the oracle with something that is *not* the oracle:
+exact-rational textbook forms written per episode (tests/textbook.py),
+closed forms, cross-estimator identities, special cases and boundary
+invariants.  A dropped term, a wrong sign or index, a swapped flag or a
+transposed operand in oracle/rlscan_oracle.c fails at least one of them
+(tests/test_oracle_mutations.py plants such mistakes and checks that).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import textbook as tb
+
+from linear_recurrence_scan_amd import synth
+
+REL = 1e-12
+
+
+def close(a, b, rel=REL):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    err = np.abs(a - b) / np.maximum(1.0, np.abs(b))
+    assert err.max(initial=0.0) <= rel, f"max rel err {err.max()}"
+
+
+def rand_rollout(rng, E, T, p_term=0.2, p_trunc=0.15):
+    u = rng.random((E, T))
+    term = (u < p_term).astype(np.float32)
+    trunc = ((u >= p_term) & (u < p_term + p_trunc)).astype(np.float32)
+    r = rng.standard_normal((E, T)).astype(np.float32)
+    v = rng.standard_normal((E, T)).astype(np.float32)
+    boot = np.where(trunc.astype(bool), rng.standard_normal((E, T)), 0.0).astype(np.float32)
+    boot[:, -1] = rng.standard_normal(E).astype(np.float32)
+    return r, v, term, trunc, boot
+
+
+# ---------------------------------------------------------------------------
+# exact-rational, episode-wise textbook forms on tiny random rows
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("mode", ["trunc_2d", "no_trunc_last_value", "no_trunc_2d_stray", "none"])
+def test_gae_matches_episode_textbook(seed, mode):
+    rng = np.random.default_rng(100 + seed)
+    E, T = 3, 11
+    r, v, term, trunc, boot = rand_rollout(rng, E, T)
+    kw = dict(gamma=0.97, lambda_=0.9)
+    if mode == "trunc_2d":
+        args = dict(truncateds=trunc, bootstrap_values=boot)
+    elif mode == "no_trunc_last_value":
+        args = dict(last_value=rng.standard_normal(E).astype(np.float32))
+    elif mode == "no_trunc_2d_stray":
+        # without truncateds only the last column of bootstrap_values counts
+        stray = rng.standard_normal((E, T)).astype(np.float32)
+        args = dict(bootstrap_values=stray)
+    else:
+        args = {}
+    adv, ret = oracle.gae(r, v, term, **args, **kw)
+    want = tb.to_array(tb.gae(r, v, term, **args, **kw))
+    close(adv, want)
+    close(ret, want + v.astype(np.float64))
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6])
+def test_gae_every_flag_pattern(T):
+    """All 3^T (none / terminated / truncated) patterns on short rows."""
+    rng = np.random.default_rng(7 + T)
+    pats = list(itertools.product([0, 1, 2], repeat=T))
+    E = len(pats)
+    code = np.array(pats, dtype=np.int64).reshape(E, T)
+    term = (code == 1).astype(np.float32)
+    trunc = (code == 2).astype(np.float32)
+    r = rng.standard_normal((E, T)).astype(np.float32)
+    v = rng.standard_normal((E, T)).astype(np.float32)
+    boot = np.where(trunc.astype(bool), rng.standard_normal((E, T)), 0.0).astype(np.float32)
+    boot[:, -1] = rng.standard_normal(E).astype(np.float32)
+    adv, _ = oracle.gae(r, v, term, trunc, 0.9, 0.8, bootstrap_values=boot)
+    want = tb.to_array(tb.gae(r, v, term, trunc, 0.9, 0.8, bootstrap_values=boot))
+    close(adv, want)
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("clips", [(1.0, 1.0), (0.8, 1.3), (2.0, 0.5)])
+@pytest.mark.parametrize("mode", ["trunc_2d", "last_value", "trunc_last_value"])
+def test_vtrace_matches_episode_textbook(seed, clips, mode):
+    rng = np.random.default_rng(200 + seed)
+    E, T = 3, 10
+    r, v, term, trunc, boot = rand_rollout(rng, E, T)
+    lpt = rng.standard_normal((E, T)).astype(np.float32)
+    lpb = (lpt - 0.7 * rng.standard_normal((E, T))).astype(np.float32)
+    rho_bar, c_bar = clips
+    lv = rng.standard_normal(E).astype(np.float32)
+    if mode == "trunc_2d":
+        args = dict(truncateds=trunc, bootstrap_values=boot)
+    elif mode == "last_value":
+        args = dict(last_value=lv)
+    else:
+        # last_value with truncations: continuation 0 at interior truncated steps
+        args = dict(truncateds=trunc, last_value=lv)
+    vs, pg = oracle.vtrace(lpt, lpb, v, r, term, **args, gamma=0.95, rho_bar=rho_bar, c_bar=c_bar)
+    log_rho = lpt.astype(np.float64) - lpb.astype(np.float64)
+    w_vs, w_pg = tb.vtrace(log_rho, v, r, term, **args, gamma=0.95, rho_bar=rho_bar, c_bar=c_bar)
+    close(vs, tb.to_array(w_vs))
+    close(pg, tb.to_array(w_pg))
+
+
+def test_vtrace_single_log_ratio_array():
+    rng = np.random.default_rng(5)
+    E, T = 4, 9
+    r, v, term, trunc, boot = rand_rollout(rng, E, T)
+    lr = (0.6 * rng.standard_normal((E, T))).astype(np.float32)
+    vs, pg = oracle.vtrace(lr, None, v, r, term, trunc, 0.9, 1.0, 1.0, bootstrap_values=boot)
+    w_vs, w_pg = tb.vtrace(lr.astype(np.float64), v, r, term, trunc, 0.9, 1.0, 1.0,
+                           bootstrap_values=boot)
+    close(vs, tb.to_array(w_vs))
+    close(pg, tb.to_array(w_pg))
+
+
+def _retrace_case(rng, E, T, A, p_term=0.2, p_trunc=0.15):
+    pi = rng.random((E, T, A)) + 0.05
+    pi = (pi / pi.sum(-1, keepdims=True)).astype(np.float32)
+    mu = rng.random((E, T)).astype(np.float32) * 0.9 + 0.05
+    q = rng.standard_normal((E, T)).astype(np.float32)
+    qn = rng.standard_normal((E, T, A)).astype(np.float32)
+    act = rng.integers(0, A, size=(E, T)).astype(np.int64)
+    r = rng.standard_normal((E, T)).astype(np.float32)
+    u = rng.random((E, T))
+    term = (u < p_term).astype(np.float32)
+    trunc = ((u >= p_term) & (u < p_term + p_trunc)).astype(np.float32)
+    return pi, mu, q, qn, act, r, term, trunc
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("params", [(0.95, 1.0, 1.0), (0.7, 1.2, 0.8), (1.0, 0.5, 2.0)])
+@pytest.mark.parametrize("with_trunc", [True, False])
+def test_retrace_matches_closed_form(seed, params, with_trunc):
+    """Q_ret from the Retrace(lambda) definition sum_k gamma^{k-t} (prod_{i=t+1}^{k} c_i)
+    delta_k (the Retrace page, Sec. 2), cut at episode ends."""
+    rng = np.random.default_rng(300 + seed)
+    E, T, A = 3, 10, 4
+    pi, mu, q, qn, act, r, term, trunc = _retrace_case(rng, E, T, A)
+    lam, c_bar, rho_bar = params
+    tr = trunc if with_trunc else None
+    q_ret, adv = oracle.retrace(pi, mu, q, qn, act, r, term, tr, 0.93, lam, c_bar, rho_bar)
+    w_q, w_adv = tb.retrace(pi, mu, q, qn, act, r, term, tr, 0.93, lam, c_bar, rho_bar)
+    close(q_ret, tb.to_array(w_q))
+    close(adv, tb.to_array(w_adv))
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("lam", [0.0, 0.4, 0.95, 1.0])
+def test_lambda_returns_match_nstep_mixture(seed, lam):
+    """Forward-view lambda-return as a mixture of n-step returns, with inputs that
+    keep the caller contract (next_values = V(s_{t+1}) at continuing steps, 0 at
+    truncated steps, and = bootstrap at a continuing window end)."""
+    rng = np.random.default_rng(400 + seed)
+    E, T = 3, 9
+    r, v, term, trunc, boot = rand_rollout(rng, E, T)
+    nv = np.zeros((E, T), np.float32)
+    nv[:, :-1] = v[:, 1:]
+    nv[trunc.astype(bool)] = 0.0
+    nv[:, -1] = np.where(term[:, -1] + trunc[:, -1] > 0, nv[:, -1], boot[:, -1])
+    got = oracle.lambda_returns(r, nv, term, trunc, 0.96, lam, boot)
+    want = tb.to_array(tb.lambda_returns_mixture(r, nv, term, trunc, boot, 0.96, lam))
+    close(got, want)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("with_trunc", [True, False])
+def test_discounted_returns_match_reward_to_go(seed, with_trunc):
+    rng = np.random.default_rng(500 + seed)
+    E, T = 3, 12
+    r, v, term, trunc, boot = rand_rollout(rng, E, T)
+    tr = trunc if with_trunc else None
+    got = oracle.discounted_returns(r, term, tr, 0.9, boot)
+    want = tb.to_array(tb.discounted_returns(r, term, tr, boot, 0.9))
+    close(got, want)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("boundary", ["ends_at", "starts_at"])
+@pytest.mark.parametrize("decay", [1.0, 0.9405, 0.5])
+@pytest.mark.parametrize("seeded", [True, False])
+def test_forward_scans_match_segment_sums(seed, boundary, decay, seeded):
+    rng = np.random.default_rng(600 + seed)
+    E, T = 4, 12
+    x = rng.standard_normal((E, T)).astype(np.float32)
+    d = (rng.random((E, T)) < 0.25).astype(np.float32)
+    s = rng.standard_normal(E).astype(np.float32) if seeded else None
+    got = oracle.forward_scan(x, d, s, decay, boundary)
+    want = tb.to_array(tb.forward_segments(x, d, s, decay, boundary))
+    close(got, want)
+
+
+def test_prefix_sum_is_segmented_cumsum():
+    """Decay 1 reduces to numpy cumsum over each segment (a library routine)."""
+    rng = np.random.default_rng(11)
+    E, T = 5, 200
+    x = rng.standard_normal((E, T)).astype(np.float32)
+    d = (rng.random((E, T)) < 0.05).astype(np.float32)
+    for boundary in ("ends_at", "starts_at"):
+        got = oracle.episodic_prefix_sum(x, d, None, boundary)
+        want = np.empty((E, T))
+        for e in range(E):
+            starts = [0]
+            for t in range(1, T):
+                if (boundary == "ends_at" and d[e, t - 1]) or (boundary == "starts_at" and d[e, t]):
+                    starts.append(t)
+            starts.append(T)
+            for a, b in zip(starts[:-1], starts[1:]):
+                want[e, a:b] = np.cumsum(x[e, a:b].astype(np.float64))
+        close(got, want, 1e-13)
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+def test_gae_geometric_closed_form():
+    """Constant r, V, no dones, V(s_T) = V: delta = r - (1-gamma) V and
+    A_t = delta (1 - (gamma lambda)^{T-t}) / (1 - gamma lambda)  (paper Sec. 3.3.1)."""
+    E, T, rv, vv = 2, 1000, 0.75, -0.5
+    g, lam = np.float32(0.99), np.float32(0.95)
+    r = np.full((E, T), rv, np.float32)
+    v = np.full((E, T), vv, np.float32)
+    z = np.zeros((E, T), np.float32)
+    adv, _ = oracle.gae(r, v, z, gamma=g, lambda_=lam, last_value=np.full(E, vv, np.float32))
+    gd, ld = float(g), float(lam)
+    delta = rv + gd * vv - vv
+    t = np.arange(T)
+    want = delta * (1 - (gd * ld) ** (T - t)) / (1 - gd * ld)
+    close(adv, np.broadcast_to(want, (E, T)), 1e-11)
+
+
+def test_gae_lambda_zero_is_one_step_td():
+    rng = np.random.default_rng(3)
+    E, T = 4, 50
+    r, v, term, trunc, boot = rand_rollout(rng, E, T, 0.05, 0.05)
+    adv, _ = oracle.gae(r, v, term, trunc, 0.9, 0.0, bootstrap_values=boot)
+    r64, v64 = r.astype(np.float64), v.astype(np.float64)
+    vnext = np.zeros((E, T))
+    vnext[:, :-1] = v64[:, 1:]
+    vnext = np.where(trunc > 0, boot, vnext)
+    vnext[:, -1] = boot[:, -1]
+    vnext = np.where(term > 0, 0.0, vnext)
+    close(adv, r64 + 0.9 * vnext - v64, 1e-13)
+
+
+def test_discounted_closed_form():
+    """G_t = r (1 - gamma^{T-t}) / (1 - gamma) + gamma^{T-t} B_{T-1}."""
+    E, T, rv, b = 3, 5000, 0.25, 2.0
+    g = float(np.float32(0.999))
+    r = np.full((E, T), rv, np.float32)
+    z = np.zeros((E, T), np.float32)
+    boot = np.zeros((E, T), np.float32)
+    boot[:, -1] = b
+    got = oracle.discounted_returns(r, z, None, g, boot)
+    t = np.arange(T)
+    want = rv * (1 - g ** (T - t)) / (1 - g) + g ** (T - t) * b
+    close(got, np.broadcast_to(want, (E, T)), 1e-10)
+
+
+def test_lambda_returns_closed_form():
+    """Constant r, next_values = c, carry c: fixed point G* = (r + gamma(1-lambda)c)/(1-gamma lambda),
+    G_t = G* + (gamma lambda)^{T-t} (c - G*)."""
+    E, T, rv, c = 2, 800, -0.375, 1.5
+    g, lam = float(np.float32(0.99)), float(np.float32(0.9))
+    r = np.full((E, T), rv, np.float32)
+    nv = np.full((E, T), c, np.float32)
+    z = np.zeros((E, T), np.float32)
+    boot = np.zeros((E, T), np.float32)
+    boot[:, -1] = c
+    got = oracle.lambda_returns(r, nv, z, None, g, lam, boot)
+    gs = (rv + g * (1 - lam) * c) / (1 - g * lam)
+    t = np.arange(T)
+    want = gs + (g * lam) ** (T - t) * (c - gs)
+    close(got, np.broadcast_to(want, (E, T)), 1e-11)
+
+
+def test_traces_closed_form():
+    """Constant g, no dones: z_t = g (1 - k^{t+1})/(1 - k) + k^{t+1} seed, k = gamma lambda."""
+    E, T, gv = 2, 700, 0.375
+    k = float(np.float32(0.99 * 0.95))
+    x = np.full((E, T), gv, np.float32)
+    z0 = np.zeros((E, T), np.float32)
+    seed = np.array([1.0, -2.0], np.float32)
+    got = oracle.eligibility_traces(x, z0, 0.0, 0.0, seed, decay=k)
+    t = np.arange(T)
+    want = gv * (1 - k ** (t + 1)) / (1 - k) + k ** (t + 1) * seed[:, None].astype(np.float64)
+    close(got, want, 1e-11)
+
+
+def test_traces_lambda_zero_is_input():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((3, 40)).astype(np.float32)
+    d = (rng.random((3, 40)) < 0.1).astype(np.float32)
+    got = oracle.eligibility_traces(x, d, 0.99, 0.0, rng.standard_normal(3).astype(np.float32))
+    close(got, x.astype(np.float64), 0.0)
+
+
+def test_prefix_sum_of_ones_counts_position_in_episode():
+    rng = np.random.default_rng(13)
+    E, T = 3, 300
+    d = (rng.random((E, T)) < 0.03).astype(np.float32)
+    ones = np.ones((E, T), np.float32)
+    got = oracle.episodic_prefix_sum(ones, d, None, "ends_at")
+    for e in range(E):
+        pos = 0
+        for t in range(T):
+            pos = pos + 1 if (t == 0 or d[e, t - 1] == 0) else 1
+            assert got[e, t] == pos
+
+
+# ---------------------------------------------------------------------------
+# identities and special cases across estimators
+# ---------------------------------------------------------------------------
+
+def test_gae_targets_equal_lambda_returns():
+    """A + V from GAE equals the lambda-return with next_values = (1-trunc) V_{t+1} and
+    next_values[T-1] = bootstrap[T-1]  (the Returns page, Sec. 6: lambda-returns are GAE targets)."""
+    rng = np.random.default_rng(21)
+    E, T = 6, 300
+    r, v, term, trunc, boot = rand_rollout(rng, E, T, 0.02, 0.02)
+    _, ret = oracle.gae(r, v, term, trunc, 0.98, 0.9, bootstrap_values=boot)
+    nv = np.zeros((E, T), np.float32)
+    nv[:, :-1] = v[:, 1:]
+    nv = np.where(trunc > 0, 0.0, nv).astype(np.float32)
+    nv[:, -1] = boot[:, -1]
+    lr = oracle.lambda_returns(r, nv, term, trunc, 0.98, 0.9, boot)
+    close(ret, lr, 1e-12)
+
+
+def test_lambda_one_equals_discounted():
+    rng = np.random.default_rng(22)
+    E, T = 4, 400
+    r, v, term, trunc, boot = rand_rollout(rng, E, T, 0.01, 0.01)
+    a = oracle.lambda_returns(r, v, term, trunc, 0.97, 1.0, boot)
+    b = oracle.discounted_returns(r, term, trunc, 0.97, boot)
+    close(a, b, 1e-15)
+
+
+def test_lambda_zero_is_one_step_target():
+    rng = np.random.default_rng(23)
+    E, T = 4, 100
+    r, v, term, trunc, boot = rand_rollout(rng, E, T, 0.05, 0.05)
+    got = oracle.lambda_returns(r, v, term, trunc, 0.97, 0.0, boot)
+    r64, v64, b64 = (x.astype(np.float64) for x in (r, v, boot))
+    d = np.minimum(term.astype(np.float64) + trunc, 1.0)
+    want = r64 + 0.97 * (1 - d) * v64 + 0.97 * trunc.astype(np.float64) * b64
+    close(got, want, 1e-13)
+
+
+def test_lambda_returns_window_edge_prices_bootstrap_once():
+    """G_{T-1} = r + gamma V(s_T) when next_values[T-1] = bootstrap[T-1] = V(s_T) (paper Sec. 3.3.4)."""
+    rng = np.random.default_rng(24)
+    E, T = 5, 30
+    r = rng.standard_normal((E, T)).astype(np.float32)
+    nv = rng.standard_normal((E, T)).astype(np.float32)
+    vs_T = rng.standard_normal(E).astype(np.float32)
+    nv[:, -1] = vs_T
+    boot = np.zeros((E, T), np.float32)
+    boot[:, -1] = vs_T
+    z = np.zeros((E, T), np.float32)
+    got = oracle.lambda_returns(r, nv, z, None, 0.9, 0.7, boot)
+    close(got[:, -1], r[:, -1] + 0.9 * vs_T.astype(np.float64), 1e-14)
+
+
+def test_vtrace_on_policy_is_gae_lambda_one():
+    rng = np.random.default_rng(25)
+    E, T = 5, 200
+    r, v, term, trunc, boot = rand_rollout(rng, E, T, 0.02, 0.02)
+    zero = np.zeros((E, T), np.float32)
+    vs, _ = oracle.vtrace(zero, None, v, r, term, trunc, 0.97, 1.0, 1.0, bootstrap_values=boot)
+    adv, _ = oracle.gae(r, v, term, trunc, 0.97, 1.0, bootstrap_values=boot)
+    close(vs, adv + v.astype(np.float64), 1e-12)
+
+
+def test_vtrace_telescoping_sum():
+    """vs_t - V_t = sum_k gamma^{k-t} (prod_{i=t}^{k-1} c_i) rho_k delta_k on one episode
+    with no dones (paper Sec. 3.3.2), evaluated in float64 with explicit loops."""
+    rng = np.random.default_rng(26)
+    T = 60
+    r = rng.standard_normal((1, T)).astype(np.float32)
+    v = rng.standard_normal((1, T)).astype(np.float32)
+    lr = (0.5 * rng.standard_normal((1, T))).astype(np.float32)
+    lv = np.array([0.3], np.float32)
+    z = np.zeros((1, T), np.float32)
+    vs, _ = oracle.vtrace(lr, None, v, r, z, None, 0.95, 1.0, 0.9, last_value=lv)
+    ratio = np.exp(lr[0].astype(np.float64))
+    rho, c = np.minimum(1.0, ratio), np.minimum(0.9, ratio)
+    vn = np.append(v[0, 1:].astype(np.float64), float(lv[0]))
+    delta = r[0].astype(np.float64) + 0.95 * vn - v[0].astype(np.float64)
+    for t in (0, 17, 59):
+        s, w = 0.0, 1.0
+        for k in range(t, T):
+            if k > t:
+                w *= 0.95 * c[k - 1]
+            s += w * rho[k] * delta[k]
+        assert abs(vs[0, t] - v[0, t] - s) <= 1e-12 * max(1.0, abs(s))
+
+
+def test_retrace_lambda_zero_is_one_step_expected_target():
+    rng = np.random.default_rng(27)
+    E, T, A = 3, 40, 5
+    pi, mu, q, qn, act, r, term, trunc = _retrace_case(rng, E, T, A, 0.05, 0.05)
+    q_ret, _ = oracle.retrace(pi, mu, q, qn, act, r, term, trunc, 0.9, 0.0)
+    expect = (pi.astype(np.float64) * qn.astype(np.float64)).sum(-1)
+    close(q_ret, r.astype(np.float64) + 0.9 * (1 - term.astype(np.float64)) * expect, 1e-13)
+
+
+def test_retrace_telescopes_to_n_step_return():
+    """If E_t = q_{t+1} and every c = 1, Q_ret_t = sum_k gamma^{k-t} r_k + gamma^{T-t} E_{T-1}
+    (the Retrace page, Sec. 1)."""
+    rng = np.random.default_rng(28)
+    E, T, A, a = 2, 25, 3, 1
+    q_full = rng.standard_normal((E, T + 1, A)).astype(np.float32)
+    pi = np.zeros((E, T, A), np.float32)
+    pi[:, :, a] = 1.0
+    mu = (rng.random((E, T)) * 0.5 + 0.25).astype(np.float32)
+    act = np.full((E, T), a, np.int64)
+    q = q_full[:, :T, a].copy()
+    qn = q_full[:, 1:, :].copy()
+    r = rng.standard_normal((E, T)).astype(np.float32)
+    z = np.zeros((E, T), np.float32)
+    q_ret, _ = oracle.retrace(pi, mu, q, qn, act, r, z, None, 0.9, 1.0, 1.0, 1.0)
+    for t in (0, 10, T - 1):
+        k = np.arange(t, T)
+        want = (0.9 ** (k - t) * r[:, t:].astype(np.float64)).sum(-1) + 0.9 ** (T - t) * q_full[:, T, a].astype(np.float64)
+        close(q_ret[:, t], want, 1e-12)
+
+
+def test_retrace_first_trace_weight_never_enters():
+    """c_t multiplies Delta_{t} only through beta_{t-1}: changing mu at t=0 changes rho_0
+    (so adv_0) but no Q_ret value (the Retrace page, Sec. 5)."""
+    rng = np.random.default_rng(29)
+    E, T, A = 3, 20, 4
+    pi, mu, q, qn, act, r, term, trunc = _retrace_case(rng, E, T, A, 0.0, 0.0)
+    q1, a1 = oracle.retrace(pi, mu, q, qn, act, r, term, trunc, 0.9, 0.9, 1.0, 5.0)
+    mu2 = mu.copy()
+    mu2[:, 0] *= 0.5
+    q2, a2 = oracle.retrace(pi, mu2, q, qn, act, r, term, trunc, 0.9, 0.9, 1.0, 5.0)
+    assert np.array_equal(q1, q2)
+    assert np.array_equal(a1[:, 1:], a2[:, 1:])
+    assert not np.array_equal(a1[:, 0], a2[:, 0])
+
+
+# ---------------------------------------------------------------------------
+# boundary invariants (paper Sec. 3.2 and 5.2)
+# ---------------------------------------------------------------------------
+
+def test_done_splits_row_into_independent_episodes():
+    """beta = 0 at a done step: running each episode as its own row gives identical doubles."""
+    rng = np.random.default_rng(31)
+    T = 40
+    r, v, term, trunc, boot = rand_rollout(rng, 1, T, 0.1, 0.1)
+    adv, _ = oracle.gae(r, v, term, trunc, 0.97, 0.9, bootstrap_values=boot)
+    done = np.minimum(term + trunc, 1)[0]
+    s = 0
+    for t in range(T):
+        if done[t] or t == T - 1:
+            sl = slice(s, t + 1)
+            seg, _ = oracle.gae(r[:, sl], v[:, sl], term[:, sl], trunc[:, sl], 0.97, 0.9,
+                                bootstrap_values=boot[:, sl])
+            assert np.array_equal(seg, adv[:, sl])
+            s = t + 1
+
+
+@pytest.mark.parametrize("est", ["gae", "vtrace", "retrace_qret", "lambda", "discounted"])
+def test_inputs_after_a_done_step_do_not_reach_back(est):
+    """Perturbing every input strictly after a done step t_d leaves all outputs at
+    t <= t_d bit-identical."""
+    rng = np.random.default_rng(32)
+    E, T, t_d = 4, 30, 12
+    r, v, term, trunc, boot = rand_rollout(rng, E, T, 0.0, 0.0)
+    term[:2, t_d] = 1
+    trunc[2:, t_d] = 1
+    boot[2:, t_d] = rng.standard_normal(2)
+
+    def perturb(x):
+        y = x.copy()
+        y[:, t_d + 1:] = rng.standard_normal(y[:, t_d + 1:].shape)
+        return y.astype(x.dtype)
+
+    def run(r, v, term, trunc, boot):
+        if est == "gae":
+            return oracle.gae(r, v, term, trunc, 0.97, 0.9, bootstrap_values=boot)
+        if est == "vtrace":
+            lr = np.sin(np.arange(E * T, dtype=np.float32)).reshape(E, T) * 0.5
+            return oracle.vtrace(lr, None, v, r, term, trunc, 0.97, 1.0, 1.0, bootstrap_values=boot)
+        if est == "retrace_qret":
+            A = 3
+            pi = np.full((E, T, A), 1.0 / A, np.float32)
+            mu = np.full((E, T), 0.5, np.float32)
+            qn = np.repeat(v[:, :, None], A, axis=2)
+            act = np.zeros((E, T), np.int64)
+            return (oracle.retrace(pi, mu, v, qn, act, r, term, trunc, 0.97, 0.9)[0],)
+        if est == "lambda":
+            return (oracle.lambda_returns(r, v, term, trunc, 0.97, 0.9, boot),)
+        return (oracle.discounted_returns(r, term, trunc, 0.97, boot),)
+
+    base = run(r, v, term, trunc, boot)
+    flags_term, flags_trunc = term.copy(), trunc.copy()
+    flags_term[:, t_d + 1:] = (rng.random((E, T - t_d - 1)) < 0.2)
+    pert = run(perturb(r), perturb(v), flags_term, flags_trunc, perturb(boot))
+    for a, b in zip(base, pert):
+        assert np.array_equal(a[:, :t_d + 1], b[:, :t_d + 1])
+
+
+def test_window_bootstrap_enters_once():
+    """Raising B_{T-1} by b changes A_t by gamma (gamma lambda)^{T-1-t} b inside the last
+    episode and nowhere else (A_T = 0; the GAE page, Sec. 5)."""
+    rng = np.random.default_rng(33)
+    E, T, g, lam, b = 3, 50, 0.97, 0.9, 0.625
+    r, v, term, trunc, boot = rand_rollout(rng, E, T, 0.03, 0.03)
+    term[:, -1] = 0
+    trunc[:, -1] = 0
+    a1, _ = oracle.gae(r, v, term, trunc, g, lam, bootstrap_values=boot)
+    boot2 = boot.copy()
+    boot2[:, -1] += b
+    a2, _ = oracle.gae(r, v, term, trunc, g, lam, bootstrap_values=boot2)
+    done = np.minimum(term + trunc, 1)
+    for e in range(E):
+        idx = np.nonzero(done[e])[0]
+        start = idx[-1] + 1 if len(idx) else 0
+        t = np.arange(T)
+        want = np.where(t >= start, g * (g * lam) ** (T - 1 - t) * b, 0.0)
+        assert np.allclose(a2[e] - a1[e], want, rtol=1e-9, atol=1e-12)
+
+
+def test_truncated_last_column_has_no_carry():
+    rng = np.random.default_rng(34)
+    E, T = 4, 20
+    r, v, term, trunc, boot = rand_rollout(rng, E, T, 0.0, 0.0)
+    trunc[:, -1] = 1
+    adv, _ = oracle.gae(r, v, term, trunc, 0.9, 0.8, bootstrap_values=boot)
+    close(adv[:, -1], r[:, -1] + 0.9 * boot[:, -1].astype(np.float64) - v[:, -1], 1e-15)
+
+
+def test_forward_split_window_chaining():
+    """C over [0, T) equals two chained calls with seed_2 = C_1[T1-1] (1 - d_{T1-1})."""
+    rng = np.random.default_rng(35)
+    E, T, T1 = 3, 60, 23
+    x = rng.standard_normal((E, T)).astype(np.float32)
+    d = (rng.random((E, T)) < 0.1).astype(np.float32)
+    s = rng.standard_normal(E).astype(np.float32)
+    full = oracle.eligibility_traces(x, d, 0.9, 0.9, s, decay=0.81)
+    c1 = oracle.eligibility_traces(x[:, :T1], d[:, :T1], 0.9, 0.9, s, decay=0.81)
+    seed2 = (c1[:, -1] * (1 - d[:, T1 - 1])).astype(np.float32)
+    c2 = oracle.eligibility_traces(x[:, T1:], d[:, T1:], 0.9, 0.9, seed2, decay=0.81)
+    close(full[:, :T1], c1, 0.0)
+    close(full[:, T1:], c2, 1e-6)   # seed2 rounded to fp32 at the API boundary
+
+
+def test_synthetic_configs_are_well_formed():
+    """Flags are 0/1 and mutually exclusive; bootstrap sits only at truncated steps and
+    the last column."""
+    d = synth.gae_trunc(E=64, T=256)
+    te, tr, b = d["terminateds"], d["truncateds"], d["bootstrap_values"]
+    assert set(np.unique(te)) <= {0.0, 1.0} and set(np.unique(tr)) <= {0.0, 1.0}
+    assert not np.any((te > 0) & (tr > 0))
+    interior = np.ones_like(b, bool)
+    interior[:, -1] = False
+    assert not np.any((b != 0) & (tr == 0) & interior)
+    rt = synth.retrace_inputs(E=4, T=16, A=18)
+    assert np.all(rt["actions"] >= 0) and np.all(rt["actions"] < 18)
+    assert np.allclose(rt["pi_target"].sum(-1), 1.0, atol=1e-5)
