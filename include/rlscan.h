@@ -1,0 +1,216 @@
+/*
+ * rlscan.h -- C ABI of librlscan.so: fused first-order linear-recurrence
+ * scans A_t = alpha_t + beta_t * A_{t+1} (backward) and
+ * A_t = alpha_t + beta_t * A_{t-1} (forward) over [num_envs, seq_len] fp32
+ * rollout buffers on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (rl-triton pages): the arXiv paper "rl-triton: High-Performance
+ * Triton GPU Kernels for Reinforcement Learning Credit Assignment" (Eq. 1-2,
+ * Table 1, Sec. 3.2-3.3) and the "rl-triton kernels" documentation page (API
+ * Reference of the seven compute_* functions).  Each entry point cites the
+ * passage that defines its operation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array pointer is a DEVICE pointer owned by the caller; nothing is
+ *   retained after the call returns.  Arrays are row-major and contiguous:
+ *   element (e, t) of an [E, T] array sits at index e*T + t.  Retrace's 3-D
+ *   arrays are [E, T, A] with element (e, t, a) at (e*T + t)*A + a.
+ * - Float arrays are fp32.  Flags (terminateds, truncateds, dones) hold
+ *   exactly 0.0f or 1.0f; done_t = min(term_t + trunc_t, 1).  Inputs must be
+ *   finite.  Outputs must not alias inputs or each other.
+ * - The arithmetic is fp32 (fused multiply-add allowed, any association of
+ *   the scan); results agree with a float64 sequential evaluation to about
+ *   1e-6 relative for T in the thousands (see the parity tests).
+ * - Calls only enqueue work on `stream` (NULL = the default stream): no host
+ *   synchronisation and no device allocation.  A call returns RLSCAN_OK once
+ *   its kernel is enqueued; launch failures are reported as
+ *   RLSCAN_ERR_LAUNCH.  Argument errors are detected on the host before any
+ *   HIP call and leave every buffer untouched.  rlscan_last_error() returns a
+ *   thread-local message describing the most recent failure.
+ * - Workspace: rows longer than one tile, or tiles that straddle rows, need a
+ *   small device workspace for the single-pass cross-workgroup carry
+ *   propagation (decoupled look-back).  rlscan_workspace_bytes(E, T) gives a
+ *   size that suffices for every entry point at that shape.  The workspace
+ *   must be zero-filled once before its first use (rlscan_workspace_init);
+ *   afterwards each call leaves it ready for the next one, so it needs no
+ *   clearing between calls and the calls are safe to record in a HIP graph.
+ *   Calls that share one workspace must be ordered (same stream, or
+ *   synchronised); concurrent calls on one workspace race.  Passing NULL /
+ *   0 is allowed when the call needs no workspace; when it does,
+ *   RLSCAN_ERR_WORKSPACE is returned.
+ */
+#ifndef RLSCAN_H
+#define RLSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RLSCAN_ABI_VERSION 1
+
+typedef struct ihipStream_t* rlscan_stream_t; /* same type as hipStream_t */
+
+typedef enum rlscan_status {
+    RLSCAN_OK = 0,
+    RLSCAN_ERR_NULL_ARG = 1,  /* a required pointer is NULL */
+    RLSCAN_ERR_BAD_SHAPE = 2, /* E, T or A out of range, or a size overflows */
+    RLSCAN_ERR_BAD_PARAM = 3, /* a scalar or enum argument is invalid */
+    RLSCAN_ERR_CONFLICT = 4,  /* mutually exclusive optional arguments were both given */
+    RLSCAN_ERR_WORKSPACE = 5, /* the call needs a workspace and none or too small a one was given */
+    RLSCAN_ERR_LAUNCH = 6     /* the HIP runtime refused the kernel launch */
+} rlscan_status;
+
+typedef enum rlscan_boundary {
+    RLSCAN_ENDS_AT = 0,  /* dones[t] = 1 ends a segment at t; the reset lands at t + 1 */
+    RLSCAN_STARTS_AT = 1 /* dones[t] = 1 starts a segment at t; the reset lands at t */
+} rlscan_boundary;
+
+/* Version of this ABI (RLSCAN_ABI_VERSION of the built library). */
+int rlscan_abi_version(void);
+
+/* Static description of a status code.  Never NULL. */
+const char* rlscan_status_string(rlscan_status status);
+
+/* Thread-local message for the most recent failing call on this thread
+ * ("" if none).  Valid until the next rlscan call on the same thread. */
+const char* rlscan_last_error(void);
+
+/* Bytes of workspace that suffice for any entry point at this shape (the
+ * Retrace entry point uses the same bound).  Returns 0 for E < 1 or T < 1. */
+size_t rlscan_workspace_bytes(int64_t num_envs, int64_t seq_len);
+
+/* Zero-fill a workspace (enqueued on `stream`, with a fill kernel so the call
+ * may be captured in a graph).  Needed once per workspace, before its first
+ * use.  `ws` must be 256-byte aligned. */
+rlscan_status rlscan_workspace_init(void* ws, size_t ws_bytes, rlscan_stream_t stream);
+
+/* Reads back the workspace's error word (synchronous: waits for `stream`).
+ * Non-zero means a look-back wait exceeded its bound and the affected
+ * outputs are invalid; the word is sticky until rlscan_workspace_init. */
+rlscan_status rlscan_workspace_error(const void* ws, uint32_t* error_out, rlscan_stream_t stream);
+
+/*
+ * GAE -- rl-triton kernels page, API Reference: compute_gae (Recurrence);
+ * paper Sec. 3.3.1, Table 1 and Sec. 3.2.
+ *   v_next_t = (1 - trunc_t) V_{t+1} + B_t  (t < T-1),   v_next_{T-1} = B_{T-1}
+ *   delta_t  = r_t + gamma (1 - term_t) v_next_t - V_t
+ *   A_t      = delta_t + gamma lambda (1 - done_t) A_{t+1},   A_T = 0
+ *   returns_t = A_t + V_t
+ * Inputs  rewards, values, terminateds: [E,T].  truncateds: [E,T] or NULL
+ *         (no truncations).  bootstrap_values: [E,T] or NULL; with
+ *         truncateds every entry is used (nonzero only at truncated steps
+ *         and column T-1 by contract), without truncateds only column T-1 is
+ *         read.  last_value: [E] or NULL, fills column T-1 (B_{T-1}).
+ * Outputs advantages [E,T]; returns [E,T] or NULL to skip.
+ * Errors  NULL required pointer -> NULL_ARG; E < 1 or T < 1 -> BAD_SHAPE;
+ *         last_value together with bootstrap_values or truncateds -> CONFLICT.
+ */
+rlscan_status rlscan_gae(const float* rewards, const float* values, const float* terminateds,
+                         const float* truncateds, const float* bootstrap_values,
+                         const float* last_value, float* advantages, float* returns,
+                         int64_t num_envs, int64_t seq_len, float gamma, float lambda,
+                         void* ws, size_t ws_bytes, rlscan_stream_t stream);
+
+/*
+ * V-trace -- kernels page, API Reference: compute_vtrace (Recurrence,
+ * Outputs); paper Sec. 3.3.2 and Table 1.
+ *   rho_hat_t = exp(log_pi_target_t - log_pi_behavior_t)
+ *   rho_t = min(rho_bar, rho_hat_t),  c_t = min(c_bar, rho_hat_t)
+ *   Delta_t = rho_t (r_t + gamma (1 - term_t) v_next_t - V_t)
+ *             + gamma c_t (1 - done_t) Delta_{t+1},   Delta_T = 0
+ *   vs_t = Delta_t + V_t
+ *   vs_next_t = (1 - trunc_t) vs_{t+1} + B_t (t < T-1),  vs_next_{T-1} = B_{T-1}
+ *   pg_t = rho_t (r_t + gamma (1 - term_t) vs_next_t - V_t)
+ * v_next_t and B_t are built as for GAE, except that last_value may be
+ * combined with truncateds (then B is last_value at t = T-1 and 0 elsewhere).
+ * Inputs  log_pi_target [E,T]; log_pi_behavior [E,T] or NULL, in which case
+ *         log_pi_target already holds log(pi/mu).  values, rewards,
+ *         terminateds [E,T] (values BEFORE rewards, as in the reference
+ *         signature); truncateds, bootstrap_values [E,T] or NULL;
+ *         last_value [E] or NULL.
+ * Outputs vs [E,T]; pg_advantages [E,T] or NULL to skip.
+ * Errors  NULL_ARG, BAD_SHAPE as above; last_value with bootstrap_values ->
+ *         CONFLICT; rho_bar or c_bar NaN -> BAD_PARAM.
+ */
+rlscan_status rlscan_vtrace(const float* log_pi_target, const float* log_pi_behavior,
+                            const float* values, const float* rewards,
+                            const float* terminateds, const float* truncateds,
+                            const float* bootstrap_values, const float* last_value,
+                            float* vs, float* pg_advantages, int64_t num_envs, int64_t seq_len,
+                            float gamma, float rho_bar, float c_bar, void* ws, size_t ws_bytes,
+                            rlscan_stream_t stream);
+
+/*
+ * Retrace(lambda) -- kernels page, API Reference: compute_retrace
+ * (Recurrence and body); paper Sec. 3.3.3; Retrace page Sec. 2-4 and 6.
+ *   E_t     = sum_a pi_target[t,a] * next_q_all[t,a]
+ *   ratio_t = pi_target[t, a_t] / mu_taken_t
+ *   c_t = lambda min(c_bar, ratio_t),   rho_t = min(rho_bar, ratio_t)
+ *   Delta_t = (r_t + gamma (1 - term_t) E_t - q_t)
+ *             + gamma c_{t+1} (1 - done_t) Delta_{t+1},   c_T = 0, Delta_T = 0
+ *   q_ret_t = Delta_t + q_t
+ *   adv_t   = rho_t (r_t + gamma (1 - term_t) q_ret_{t+1} - q_t),   q_ret_T = 0
+ * Inputs  pi_target, next_q_all: [E,T,A]; mu_taken, q_taken, rewards,
+ *         terminateds: [E,T]; actions: int64 [E,T] with values in [0, A)
+ *         (an out-of-range action is clamped into range for memory safety,
+ *         and its outputs are then meaningless); truncateds [E,T] or NULL
+ *         (no truncations).  mu_taken must be > 0.
+ * Outputs q_ret [E,T]; advantages [E,T] or NULL to skip.
+ * Errors  NULL_ARG; BAD_SHAPE for E, T < 1 or A outside [1, 128].
+ */
+rlscan_status rlscan_retrace(const float* pi_target, const float* mu_taken, const float* q_taken,
+                             const float* next_q_all, const int64_t* actions,
+                             const float* rewards, const float* terminateds,
+                             const float* truncateds, float* q_ret, float* advantages,
+                             int64_t num_envs, int64_t seq_len, int64_t num_actions, float gamma,
+                             float lambda, float c_bar, float rho_bar, void* ws, size_t ws_bytes,
+                             rlscan_stream_t stream);
+
+/*
+ * TD(lambda) and discounted returns -- kernels page, API Reference:
+ * compute_lambda_returns and compute_discounted_returns (Recurrence and
+ * chunked bodies); paper Sec. 3.3.4 and Table 1.
+ *   G_t = r_t + gamma (1 - lambda)(1 - done_t) NV_t + gamma trunc_t B_t
+ *         + gamma lambda (1 - done_t) G_{t+1},          G_T = B_{T-1}
+ * With next_values == NULL this is the discounted return
+ *   G_t = r_t + gamma trunc_t B_t + gamma (1 - done_t) G_{t+1}
+ * and `lambda` is ignored (taken as 1).
+ * Inputs  rewards, terminateds [E,T]; next_values [E,T] or NULL (the caller
+ *         zeroes it at truncated steps); truncateds [E,T] or NULL;
+ *         bootstrap_values [E,T] or NULL (all zeros).
+ * Outputs out [E,T].
+ * Errors  NULL_ARG, BAD_SHAPE as above.
+ */
+rlscan_status rlscan_returns(const float* rewards, const float* next_values,
+                             const float* terminateds, const float* truncateds,
+                             const float* bootstrap_values, float* out, int64_t num_envs,
+                             int64_t seq_len, float gamma, float lambda, void* ws,
+                             size_t ws_bytes, rlscan_stream_t stream);
+
+/*
+ * Forward recurrences: eligibility traces and the episodic prefix sum --
+ * kernels page, API Reference: compute_eligibility_traces and
+ * compute_episodic_prefix_sum (Recurrence); paper Sec. 3.3.5, 3.3.6, Table 1.
+ *   RLSCAN_ENDS_AT:   C_t = x_t + decay (1 - d_{t-1}) C_{t-1},   d_{-1} = 0
+ *   RLSCAN_STARTS_AT: C_t = x_t + decay (1 - d_t) C_{t-1}
+ *   C_{-1} = seed[e] (0 when seed is NULL)
+ * Eligibility traces: decay = gamma * lambda with RLSCAN_ENDS_AT.  Prefix
+ * sum: decay = 1.
+ * Inputs  inputs, dones [E,T]; seed [E] or NULL.
+ * Outputs out [E,T].
+ * Errors  NULL_ARG, BAD_SHAPE as above; unknown boundary -> BAD_PARAM.
+ */
+rlscan_status rlscan_prefix(const float* inputs, const float* dones, const float* seed, float* out,
+                            int64_t num_envs, int64_t seq_len, float decay,
+                            rlscan_boundary boundary, void* ws, size_t ws_bytes,
+                            rlscan_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLSCAN_H */

@@ -1,0 +1,292 @@
+// rlscan_api.cpp -- the C ABI of librlscan.so: argument validation (host
+// only, before any HIP call), launch planning, and dispatch to the kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "rlscan_internal.hpp"
+
+namespace rlscan {
+
+namespace {
+thread_local char g_last_error[512] = "";
+
+bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Tile size override for tuning experiments: RLSCAN_TILE=256|1024|4096.
+int tile_override() {
+    static int cached = -1;
+    if (cached < 0) {
+        const char* s = std::getenv("RLSCAN_TILE");
+        int v = s ? std::atoi(s) : 0;
+        cached = (v == 256 || v == 1024 || v == 4096) ? v : 0;
+    }
+    return cached;
+}
+
+constexpr int64_t kMaxTiles = (int64_t)1 << 31;
+constexpr int kMinTile = 256;
+
+size_t ws_bytes_for_tiles(int64_t tiles) {
+    return (size_t)WsHeader::kSlotsByteOffset + (size_t)tiles * 32u;
+}
+
+// Plans a launch of a 4-elements-per-lane kernel.
+rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
+    const int64_t N = E * T;
+    int tile = tile_override();
+    if (tile == 0) {
+        if (T >= 4096) tile = 4096;
+        else if (N <= (int64_t)256 * 1024) tile = 256;
+        else tile = 1024;
+    }
+    plan.tile = tile;
+    plan.waves = tile == 4096 ? 4 : 1;
+    plan.geo.N = N;
+    plan.geo.T = T;
+    plan.geo.num_tiles = (N + tile - 1) / tile;
+    plan.geo.magic = T < tile ? (uint32_t)(0xFFFFFFFFu / (uint32_t)T) : 0u;
+    plan.geo.vec_ok = vec_ok ? 1 : 0;
+    plan.lookback = plan.geo.num_tiles > 1 && (tile % T) != 0;
+    if (plan.geo.num_tiles >= kMaxTiles) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
+    return RLSCAN_OK;
+}
+
+rlscan_status plan_retrace(int64_t E, int64_t T, int64_t A, Plan& plan, bool vec_ok) {
+    const int64_t N = E * T;
+    int tile = 1024, waves = 4;
+    if (A > 32) waves = 1;  // 2*64*A floats of LDS per wave
+    if (N <= (int64_t)64 * 1024) {
+        tile = 256;
+        waves = 1;
+    }
+    plan.tile = tile;
+    plan.waves = waves;
+    plan.geo.N = N;
+    plan.geo.T = T;
+    plan.geo.num_tiles = (N + tile - 1) / tile;
+    plan.geo.magic = T < tile ? (uint32_t)(0xFFFFFFFFu / (uint32_t)T) : 0u;
+    plan.geo.vec_ok = vec_ok ? 1 : 0;
+    plan.lookback = plan.geo.num_tiles > 1 && (tile % T) != 0;
+    if (plan.geo.num_tiles >= kMaxTiles) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
+    return RLSCAN_OK;
+}
+
+rlscan_status check_shape(int64_t E, int64_t T) {
+    if (E < 1 || T < 1) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs and seq_len must be >= 1");
+    if (T > ((int64_t)1 << 40) || E > ((int64_t)1 << 40) || E > (((int64_t)1 << 46) / T))
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
+    return RLSCAN_OK;
+}
+
+rlscan_status check_ws(const Plan& plan, void* ws, size_t ws_bytes) {
+    if (!plan.lookback) return RLSCAN_OK;
+    if (!ws) return set_error(RLSCAN_ERR_WORKSPACE, "this shape needs a workspace (rlscan_workspace_bytes)");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return set_error(RLSCAN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < ws_bytes_for_tiles(plan.geo.num_tiles))
+        return set_error(RLSCAN_ERR_WORKSPACE, "workspace too small (rlscan_workspace_bytes)");
+    return RLSCAN_OK;
+}
+
+#define RLSCAN_REQUIRE(ptr, name)                                                  \
+    do {                                                                          \
+        if (!(ptr)) return set_error(RLSCAN_ERR_NULL_ARG, name " must not be NULL"); \
+    } while (0)
+
+#define RLSCAN_TRY(expr)                       \
+    do {                                       \
+        const rlscan_status st_ = (expr);      \
+        if (st_ != RLSCAN_OK) return st_;      \
+    } while (0)
+
+}  // namespace
+
+rlscan_status set_error(rlscan_status st, const char* msg) {
+    std::snprintf(g_last_error, sizeof(g_last_error), "%s", msg ? msg : "");
+    return st;
+}
+
+}  // namespace rlscan
+
+using namespace rlscan;
+
+extern "C" {
+
+int rlscan_abi_version(void) { return RLSCAN_ABI_VERSION; }
+
+const char* rlscan_status_string(rlscan_status status) {
+    switch (status) {
+        case RLSCAN_OK: return "ok";
+        case RLSCAN_ERR_NULL_ARG: return "a required pointer is NULL";
+        case RLSCAN_ERR_BAD_SHAPE: return "invalid shape";
+        case RLSCAN_ERR_BAD_PARAM: return "invalid parameter";
+        case RLSCAN_ERR_CONFLICT: return "conflicting optional arguments";
+        case RLSCAN_ERR_WORKSPACE: return "missing or too small workspace";
+        case RLSCAN_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+const char* rlscan_last_error(void) { return g_last_error; }
+
+size_t rlscan_workspace_bytes(int64_t num_envs, int64_t seq_len) {
+    if (num_envs < 1 || seq_len < 1 || check_shape(num_envs, seq_len) != RLSCAN_OK) return 0;
+    const int64_t N = num_envs * seq_len;
+    return ws_bytes_for_tiles((N + kMinTile - 1) / kMinTile);
+}
+
+rlscan_status rlscan_workspace_init(void* ws, size_t ws_bytes, rlscan_stream_t stream) {
+    RLSCAN_REQUIRE(ws, "ws");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return set_error(RLSCAN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < (size_t)WsHeader::kSlotsByteOffset)
+        return set_error(RLSCAN_ERR_WORKSPACE, "workspace smaller than its header");
+    return launch_fill_zero(ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+}
+
+rlscan_status rlscan_workspace_error(const void* ws, uint32_t* error_out, rlscan_stream_t stream) {
+    RLSCAN_REQUIRE(ws, "ws");
+    RLSCAN_REQUIRE(error_out, "error_out");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t err = hipStreamSynchronize(s);
+    if (err == hipSuccess)
+        err = hipMemcpy(error_out, static_cast<const uint8_t*>(ws) + 4 * WsHeader::kError,
+                        sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
+    return RLSCAN_OK;
+}
+
+rlscan_status rlscan_gae(const float* rewards, const float* values, const float* terminateds,
+                         const float* truncateds, const float* bootstrap_values,
+                         const float* last_value, float* advantages, float* returns,
+                         int64_t num_envs, int64_t seq_len, float gamma, float lambda, void* ws,
+                         size_t ws_bytes, rlscan_stream_t stream) {
+    RLSCAN_REQUIRE(rewards, "rewards");
+    RLSCAN_REQUIRE(values, "values");
+    RLSCAN_REQUIRE(terminateds, "terminateds");
+    RLSCAN_REQUIRE(advantages, "advantages");
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (last_value && bootstrap_values)
+        return set_error(RLSCAN_ERR_CONFLICT, "pass either last_value or bootstrap_values, not both");
+    if (last_value && truncateds)
+        return set_error(RLSCAN_ERR_CONFLICT, "last_value cannot be combined with truncateds; use bootstrap_values");
+    if (std::isnan(gamma) || std::isnan(lambda)) return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN");
+    const bool vec = aligned16(rewards) && aligned16(values) && aligned16(terminateds) &&
+                     aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(advantages) &&
+                     aligned16(returns);
+    Plan plan;
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
+    GaeArgs a{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+              advantages, returns, gamma, lambda};
+    return launch_gae(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+rlscan_status rlscan_vtrace(const float* log_pi_target, const float* log_pi_behavior,
+                            const float* values, const float* rewards, const float* terminateds,
+                            const float* truncateds, const float* bootstrap_values,
+                            const float* last_value, float* vs, float* pg_advantages,
+                            int64_t num_envs, int64_t seq_len, float gamma, float rho_bar,
+                            float c_bar, void* ws, size_t ws_bytes, rlscan_stream_t stream) {
+    RLSCAN_REQUIRE(log_pi_target, "log_pi_target");
+    RLSCAN_REQUIRE(values, "values");
+    RLSCAN_REQUIRE(rewards, "rewards");
+    RLSCAN_REQUIRE(terminateds, "terminateds");
+    RLSCAN_REQUIRE(vs, "vs");
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (last_value && bootstrap_values)
+        return set_error(RLSCAN_ERR_CONFLICT, "pass either last_value or bootstrap_values, not both");
+    if (std::isnan(gamma) || std::isnan(rho_bar) || std::isnan(c_bar))
+        return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/rho_bar/c_bar is NaN");
+    const bool vec = aligned16(log_pi_target) && aligned16(log_pi_behavior) && aligned16(values) &&
+                     aligned16(rewards) && aligned16(terminateds) && aligned16(truncateds) &&
+                     aligned16(bootstrap_values) && aligned16(vs) && aligned16(pg_advantages);
+    Plan plan;
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
+    VtraceArgs a{log_pi_target, log_pi_behavior, values, rewards, terminateds, truncateds,
+                 bootstrap_values, last_value, vs, pg_advantages, gamma, rho_bar, c_bar};
+    return launch_vtrace(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+rlscan_status rlscan_retrace(const float* pi_target, const float* mu_taken, const float* q_taken,
+                             const float* next_q_all, const int64_t* actions, const float* rewards,
+                             const float* terminateds, const float* truncateds, float* q_ret,
+                             float* advantages, int64_t num_envs, int64_t seq_len,
+                             int64_t num_actions, float gamma, float lambda, float c_bar,
+                             float rho_bar, void* ws, size_t ws_bytes, rlscan_stream_t stream) {
+    RLSCAN_REQUIRE(pi_target, "pi_target");
+    RLSCAN_REQUIRE(mu_taken, "mu_taken");
+    RLSCAN_REQUIRE(q_taken, "q_taken");
+    RLSCAN_REQUIRE(next_q_all, "next_q_all");
+    RLSCAN_REQUIRE(actions, "actions");
+    RLSCAN_REQUIRE(rewards, "rewards");
+    RLSCAN_REQUIRE(terminateds, "terminateds");
+    RLSCAN_REQUIRE(q_ret, "q_ret");
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (num_actions < 1 || num_actions > 128)
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_actions must lie in [1, 128]");
+    if (std::isnan(gamma) || std::isnan(lambda) || std::isnan(c_bar) || std::isnan(rho_bar))
+        return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda/c_bar/rho_bar is NaN");
+    const bool vec = aligned16(pi_target) && aligned16(next_q_all);
+    Plan plan;
+    RLSCAN_TRY(plan_retrace(num_envs, seq_len, num_actions, plan, vec));
+    RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
+    RetraceArgs a{pi_target, mu_taken, q_taken, next_q_all, actions, rewards, terminateds,
+                  truncateds, q_ret, advantages, num_actions, gamma, lambda, c_bar, rho_bar};
+    return launch_retrace(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+rlscan_status rlscan_returns(const float* rewards, const float* next_values,
+                             const float* terminateds, const float* truncateds,
+                             const float* bootstrap_values, float* out, int64_t num_envs,
+                             int64_t seq_len, float gamma, float lambda, void* ws, size_t ws_bytes,
+                             rlscan_stream_t stream) {
+    RLSCAN_REQUIRE(rewards, "rewards");
+    RLSCAN_REQUIRE(terminateds, "terminateds");
+    RLSCAN_REQUIRE(out, "out");
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (std::isnan(gamma) || std::isnan(lambda)) return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN");
+    const bool vec = aligned16(rewards) && aligned16(next_values) && aligned16(terminateds) &&
+                     aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(out);
+    Plan plan;
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
+    ReturnsArgs a{rewards, next_values, terminateds, truncateds, bootstrap_values, out, gamma, lambda};
+    return launch_returns(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+rlscan_status rlscan_prefix(const float* inputs, const float* dones, const float* seed, float* out,
+                            int64_t num_envs, int64_t seq_len, float decay,
+                            rlscan_boundary boundary, void* ws, size_t ws_bytes,
+                            rlscan_stream_t stream) {
+    RLSCAN_REQUIRE(inputs, "inputs");
+    RLSCAN_REQUIRE(dones, "dones");
+    RLSCAN_REQUIRE(out, "out");
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (boundary != RLSCAN_ENDS_AT && boundary != RLSCAN_STARTS_AT)
+        return set_error(RLSCAN_ERR_BAD_PARAM, "boundary must be RLSCAN_ENDS_AT or RLSCAN_STARTS_AT");
+    if (std::isnan(decay)) return set_error(RLSCAN_ERR_BAD_PARAM, "decay is NaN");
+    const bool vec = aligned16(inputs) && aligned16(dones) && aligned16(out);
+    Plan plan;
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
+    PrefixArgs a{inputs, dones, seed, out, decay, boundary == RLSCAN_STARTS_AT ? 1 : 0};
+    return launch_prefix(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+rlscan_status rlscan_debug_wave_scan(const float* a, const float* b, float* out_a, float* out_b,
+                                     int num_waves, rlscan_stream_t stream) {
+    RLSCAN_REQUIRE(a, "a");
+    RLSCAN_REQUIRE(b, "b");
+    RLSCAN_REQUIRE(out_a, "out_a");
+    RLSCAN_REQUIRE(out_b, "out_b");
+    if (num_waves < 1 || num_waves > 65535) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_waves out of range");
+    return launch_debug_wave_scan(a, b, out_a, out_b, num_waves, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

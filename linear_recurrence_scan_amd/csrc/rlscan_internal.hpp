@@ -1,0 +1,69 @@
+// rlscan_internal.hpp -- declarations shared by the host API (rlscan_api.cpp)
+// and the kernels (rlscan_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rlscan.h"
+#include "../../include/rlscan_debug.h"
+#include "scan_core.hpp"
+
+namespace rlscan {
+
+struct GaeArgs {
+    const float *rewards, *values, *terminateds, *truncateds, *bootstrap_values, *last_value;
+    float *advantages, *returns;
+    float gamma, lambda;
+};
+
+struct VtraceArgs {
+    const float *log_pi_target, *log_pi_behavior, *values, *rewards, *terminateds, *truncateds,
+        *bootstrap_values, *last_value;
+    float *vs, *pg_advantages;
+    float gamma, rho_bar, c_bar;
+};
+
+struct RetraceArgs {
+    const float *pi_target, *mu_taken, *q_taken, *next_q_all;
+    const int64_t* actions;
+    const float *rewards, *terminateds, *truncateds;
+    float *q_ret, *advantages;
+    int64_t A;
+    float gamma, lambda, c_bar, rho_bar;
+};
+
+struct ReturnsArgs {
+    const float *rewards, *next_values, *terminateds, *truncateds, *bootstrap_values;
+    float* out;
+    float gamma, lambda;
+};
+
+struct PrefixArgs {
+    const float *inputs, *dones, *seed;
+    float* out;
+    float decay;
+    int starts_at;
+};
+
+// Launch plan chosen on the host.
+struct Plan {
+    Geo geo;
+    int tile;       // elements per workgroup
+    int waves;      // waves per workgroup
+    bool lookback;  // cross-workgroup carries needed
+};
+
+rlscan_status set_error(rlscan_status st, const char* msg);
+
+rlscan_status launch_gae(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
+rlscan_status launch_vtrace(const VtraceArgs& a, const Plan& plan, void* ws, hipStream_t s);
+rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s);
+rlscan_status launch_returns(const ReturnsArgs& a, const Plan& plan, void* ws, hipStream_t s);
+rlscan_status launch_prefix(const PrefixArgs& a, const Plan& plan, void* ws, hipStream_t s);
+rlscan_status launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+rlscan_status launch_debug_wave_scan(const float* a, const float* b, float* oa, float* ob,
+                                    int num_waves, hipStream_t s);
+
+}  // namespace rlscan

@@ -1,0 +1,328 @@
+"""Thin ctypes binding over librlscan.so (C ABI in include/rlscan.h).
+
+Argument marshalling only: every step of every estimator runs in the HIP
+kernels.  PyTorch provides device memory (outputs, the cached look-back
+workspace) and the current stream.  There is no CPU fallback: a missing
+library or a tensor that is not on a GPU raises.
+
+Two layers, same names as the C ABI plus the reference-style helpers:
+  * rlscan_gae / rlscan_vtrace / rlscan_retrace / rlscan_returns /
+    rlscan_prefix: mirror the C signatures on tensors (None for NULL) and
+    write into caller-provided outputs;
+  * gae / vtrace / retrace / lambda_returns / discounted_returns /
+    eligibility_traces / episodic_prefix_sum: allocate outputs and follow the
+    rl-triton keyword conventions (kernels page, API Reference).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librlscan.so")
+
+RLSCAN_OK = 0
+RLSCAN_ENDS_AT = 0
+RLSCAN_STARTS_AT = 1
+
+_lib = None
+_lock = threading.Lock()
+_workspaces: dict = {}
+
+
+class RLScanError(RuntimeError):
+    def __init__(self, func, status, message):
+        self.status = status
+        super().__init__(f"{func} failed: status {status} ({message})")
+
+
+def lib():
+    """Loads librlscan.so once (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(f"{LIB_PATH} is not built; run "
+                                       "`python -m linear_recurrence_scan_amd.build`")
+                _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def _declare(L):
+    vp, i64, f32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    st = ctypes.c_int
+    L.rlscan_abi_version.restype = ctypes.c_int
+    L.rlscan_status_string.argtypes = [st]
+    L.rlscan_status_string.restype = ctypes.c_char_p
+    L.rlscan_last_error.restype = ctypes.c_char_p
+    L.rlscan_workspace_bytes.argtypes = [i64, i64]
+    L.rlscan_workspace_bytes.restype = sz
+    L.rlscan_workspace_init.argtypes = [vp, sz, vp]
+    L.rlscan_workspace_error.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
+    L.rlscan_gae.argtypes = [vp] * 8 + [i64, i64, f32, f32, vp, sz, vp]
+    L.rlscan_vtrace.argtypes = [vp] * 10 + [i64, i64, f32, f32, f32, vp, sz, vp]
+    L.rlscan_retrace.argtypes = [vp] * 10 + [i64, i64, i64, f32, f32, f32, f32, vp, sz, vp]
+    L.rlscan_returns.argtypes = [vp] * 6 + [i64, i64, f32, f32, vp, sz, vp]
+    L.rlscan_prefix.argtypes = [vp] * 4 + [i64, i64, f32, ctypes.c_int, vp, sz, vp]
+    L.rlscan_debug_wave_scan.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
+    for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error", "rlscan_gae", "rlscan_vtrace",
+                 "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
+        getattr(L, name).restype = st
+    return L
+
+
+def _check(func, status):
+    if status != RLSCAN_OK:
+        msg = lib().rlscan_last_error().decode(errors="replace")
+        raise RLScanError(func, status, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _f32(name, t, shape=None, device=None, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name}: expected float32, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
+    return t.contiguous()
+
+
+def _shape2(name, t):
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{name} must be a [num_envs, seq_len] tensor")
+    return tuple(t.shape)
+
+
+def workspace(device, num_envs, seq_len):
+    """Returns (tensor, nbytes) of a zero-initialised look-back workspace cached
+    per (device, stream); grows on demand.  Calls on one stream are ordered, so
+    sharing the workspace among them is safe."""
+    device = torch.device(device)
+    need = int(lib().rlscan_workspace_bytes(num_envs, seq_len))
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 4096), dtype=torch.uint8, device=device)
+        _check("rlscan_workspace_init", lib().rlscan_workspace_init(_ptr(ws), ws.numel(), _stream(device)))
+        _workspaces[key] = ws
+    return ws, ws.numel()
+
+
+def workspace_error(device=None):
+    """Error word of the current stream's cached workspace (0 = no look-back
+    wait ever exceeded its bound)."""
+    device = torch.device(device if device is not None else torch.cuda.current_device())
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None:
+        return 0
+    out = ctypes.c_uint32(0)
+    _check("rlscan_workspace_error", lib().rlscan_workspace_error(_ptr(ws), ctypes.byref(out),
+                                                                  _stream(device)))
+    return int(out.value)
+
+
+# ---------------------------------------------------------------------------
+# C-ABI mirrors (outputs provided by the caller)
+# ---------------------------------------------------------------------------
+
+def rlscan_gae(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+               advantages, returns, gamma, lambda_):
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    ws, nws = workspace(dev, E, T)
+    st = lib().rlscan_gae(_ptr(rewards), _ptr(values), _ptr(terminateds), _ptr(truncateds),
+                          _ptr(bootstrap_values), _ptr(last_value), _ptr(advantages), _ptr(returns),
+                          E, T, float(gamma), float(lambda_), _ptr(ws), nws, _stream(dev))
+    _check("rlscan_gae", st)
+
+
+def rlscan_vtrace(log_pi_target, log_pi_behavior, values, rewards, terminateds, truncateds,
+                  bootstrap_values, last_value, vs, pg_advantages, gamma, rho_bar, c_bar):
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    ws, nws = workspace(dev, E, T)
+    st = lib().rlscan_vtrace(_ptr(log_pi_target), _ptr(log_pi_behavior), _ptr(values), _ptr(rewards),
+                             _ptr(terminateds), _ptr(truncateds), _ptr(bootstrap_values),
+                             _ptr(last_value), _ptr(vs), _ptr(pg_advantages), E, T, float(gamma),
+                             float(rho_bar), float(c_bar), _ptr(ws), nws, _stream(dev))
+    _check("rlscan_vtrace", st)
+
+
+def rlscan_retrace(pi_target, mu_taken, q_taken, next_q_all, actions, rewards, terminateds,
+                   truncateds, q_ret, advantages, gamma, lambda_, c_bar, rho_bar):
+    E, T = _shape2("rewards", rewards)
+    A = int(pi_target.shape[-1])
+    dev = rewards.device
+    ws, nws = workspace(dev, E, T)
+    st = lib().rlscan_retrace(_ptr(pi_target), _ptr(mu_taken), _ptr(q_taken), _ptr(next_q_all),
+                              _ptr(actions), _ptr(rewards), _ptr(terminateds), _ptr(truncateds),
+                              _ptr(q_ret), _ptr(advantages), E, T, A, float(gamma), float(lambda_),
+                              float(c_bar), float(rho_bar), _ptr(ws), nws, _stream(dev))
+    _check("rlscan_retrace", st)
+
+
+def rlscan_returns(rewards, next_values, terminateds, truncateds, bootstrap_values, out, gamma,
+                   lambda_):
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    ws, nws = workspace(dev, E, T)
+    st = lib().rlscan_returns(_ptr(rewards), _ptr(next_values), _ptr(terminateds), _ptr(truncateds),
+                              _ptr(bootstrap_values), _ptr(out), E, T, float(gamma), float(lambda_),
+                              _ptr(ws), nws, _stream(dev))
+    _check("rlscan_returns", st)
+
+
+def rlscan_prefix(inputs, dones, seed, out, decay, boundary):
+    E, T = _shape2("inputs", inputs)
+    dev = inputs.device
+    ws, nws = workspace(dev, E, T)
+    b = {"ends_at": RLSCAN_ENDS_AT, "starts_at": RLSCAN_STARTS_AT}.get(boundary, boundary)
+    st = lib().rlscan_prefix(_ptr(inputs), _ptr(dones), _ptr(seed), _ptr(out), E, T, float(decay),
+                             int(b), _ptr(ws), nws, _stream(dev))
+    _check("rlscan_prefix", st)
+
+
+def rlscan_debug_wave_scan(a, b, out_a, out_b):
+    """Runs only the 64-lane affine wave scan (diagnostic; include/rlscan_debug.h)."""
+    n = a.numel() // 64
+    _check("rlscan_debug_wave_scan", lib().rlscan_debug_wave_scan(
+        _ptr(a), _ptr(b), _ptr(out_a), _ptr(out_b), n, _stream(a.device)))
+
+
+# ---------------------------------------------------------------------------
+# Reference-style helpers (allocate outputs; rl-triton keyword conventions)
+# ---------------------------------------------------------------------------
+
+def gae(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
+        bootstrap_values=None, last_value=None, want_returns=False):
+    """GAE advantages (and returns = advantages + values if want_returns)."""
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    r = _f32("rewards", rewards, (E, T))
+    v = _f32("values", values, (E, T), dev)
+    te = _f32("terminateds", terminateds, (E, T), dev)
+    tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
+    bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
+    lv = _f32("last_value", last_value, (E,), dev, optional=True)
+    adv = torch.empty_like(r)
+    ret = torch.empty_like(r) if want_returns else None
+    rlscan_gae(r, v, te, tr, bv, lv, adv, ret, gamma, lambda_)
+    return (adv, ret) if want_returns else adv
+
+
+def vtrace(log_pi_target, log_pi_behavior, values, rewards, terminateds, truncateds=None,
+           gamma=0.99, rho_bar=1.0, c_bar=1.0, bootstrap_values=None, last_value=None):
+    """V-trace targets and policy-gradient advantages.  log_pi_behavior=None means
+    log_pi_target already holds log(pi/mu)."""
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    lpt = _f32("log_pi_target", log_pi_target, (E, T), dev)
+    lpb = _f32("log_pi_behavior", log_pi_behavior, (E, T), dev, optional=True)
+    v = _f32("values", values, (E, T), dev)
+    r = _f32("rewards", rewards, (E, T))
+    te = _f32("terminateds", terminateds, (E, T), dev)
+    tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
+    bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
+    lv = _f32("last_value", last_value, (E,), dev, optional=True)
+    vs = torch.empty_like(r)
+    pg = torch.empty_like(r)
+    rlscan_vtrace(lpt, lpb, v, r, te, tr, bv, lv, vs, pg, gamma, rho_bar, c_bar)
+    return vs, pg
+
+
+def retrace(action_probs_target, action_probs_behavior, q_values, next_q_values_all, actions,
+            rewards, terminateds, truncateds=None, gamma=0.99, lambda_=1.0, c_bar=1.0, rho_bar=1.0):
+    """Retrace(lambda) targets and advantages (argument order of compute_retrace)."""
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    if not isinstance(action_probs_target, torch.Tensor) or action_probs_target.dim() != 3:
+        raise ValueError("action_probs_target must be [num_envs, seq_len, num_actions]")
+    A = int(action_probs_target.shape[2])
+    pi = _f32("action_probs_target", action_probs_target, (E, T, A), dev)
+    qn = _f32("next_q_values_all", next_q_values_all, (E, T, A), dev)
+    mu = _f32("action_probs_behavior", action_probs_behavior, (E, T), dev)
+    q = _f32("q_values", q_values, (E, T), dev)
+    r = _f32("rewards", rewards, (E, T))
+    te = _f32("terminateds", terminateds, (E, T), dev)
+    tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
+    if not isinstance(actions, torch.Tensor) or actions.dtype != torch.int64:
+        raise TypeError("actions must be an int64 tensor")
+    if tuple(actions.shape) != (E, T) or actions.device != dev:
+        raise ValueError("actions must be [num_envs, seq_len] on the same device")
+    act = actions.contiguous()
+    q_ret = torch.empty_like(r)
+    adv = torch.empty_like(r)
+    rlscan_retrace(pi, mu, q, qn, act, r, te, tr, q_ret, adv, gamma, lambda_, c_bar, rho_bar)
+    return q_ret, adv
+
+
+def lambda_returns(rewards, next_values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
+                   bootstrap_values=None):
+    """TD(lambda) returns."""
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    r = _f32("rewards", rewards, (E, T))
+    nv = _f32("next_values", next_values, (E, T), dev)
+    te = _f32("terminateds", terminateds, (E, T), dev)
+    tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
+    bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
+    out = torch.empty_like(r)
+    rlscan_returns(r, nv, te, tr, bv, out, gamma, lambda_)
+    return out
+
+
+def discounted_returns(rewards, terminateds, truncateds=None, gamma=0.99, bootstrap_values=None):
+    """Discounted returns (reward-to-go)."""
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    r = _f32("rewards", rewards, (E, T))
+    te = _f32("terminateds", terminateds, (E, T), dev)
+    tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
+    bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
+    out = torch.empty_like(r)
+    rlscan_returns(r, None, te, tr, bv, out, gamma, 1.0)
+    return out
+
+
+def _forward(inputs, dones, seed_values, decay, boundary):
+    if boundary not in ("ends_at", "starts_at"):
+        raise ValueError(f"boundary must be 'ends_at' or 'starts_at', got {boundary!r}")
+    E, T = _shape2("inputs", inputs)
+    dev = inputs.device
+    x = _f32("inputs", inputs, (E, T))
+    d = _f32("dones", dones, (E, T), dev)
+    s = _f32("seed_values", seed_values, (E,), dev, optional=True)
+    out = torch.empty_like(x)
+    rlscan_prefix(x, d, s, out, decay, boundary)
+    return out
+
+
+def eligibility_traces(gradients, dones, gamma, lambda_, seed_values=None):
+    """Accumulating eligibility traces (forward scan, decay gamma*lambda, ends_at)."""
+    return _forward(gradients, dones, seed_values, float(gamma) * float(lambda_), "ends_at")
+
+
+def episodic_prefix_sum(inputs, dones, seed_values=None, boundary="ends_at"):
+    """Cumulative sum that resets at segment boundaries."""
+    return _forward(inputs, dones, seed_values, 1.0, boundary)

@@ -1,0 +1,148 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/rlscan.h declares, and rejects bad arguments with the
+documented status codes before making any HIP call.  Pointers passed here
+are fake non-NULL host addresses; validation fails before anything could
+dereference them."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_recurrence_scan_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("rlscan.h", "rlscan_debug.h")]
+
+OK, NULL_ARG, BAD_SHAPE, BAD_PARAM, CONFLICT, WORKSPACE = 0, 1, 2, 3, 4, 5
+P = ctypes.c_void_p(0x1000)  # fake device pointer, never dereferenced
+N = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ops.LIB_PATH):
+        from linear_recurrence_scan_amd import build
+        build.build()
+    return ops.lib()
+
+
+def declared_functions():
+    text = "".join(open(h).read() for h in HEADERS)
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlscan_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("rlscan_gae", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(L):
+    for name in declared_functions():
+        assert hasattr(L, name), f"missing export {name}"
+
+
+def test_abi_version_and_strings(L):
+    assert L.rlscan_abi_version() == 1
+    for st in range(0, 7):
+        assert L.rlscan_status_string(st)
+    assert L.rlscan_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes(L):
+    assert L.rlscan_workspace_bytes(0, 10) == 0
+    assert L.rlscan_workspace_bytes(10, 0) == 0
+    small = L.rlscan_workspace_bytes(1, 1)
+    assert small >= 256
+    big = L.rlscan_workspace_bytes(64, 131072)
+    assert big >= 256 + 32 * (64 * 131072 // 1024)
+
+
+def gae(L, r=P, v=P, te=P, tr=N, bv=N, lv=N, adv=P, ret=N, E=4, T=8, ws=N, nws=0):
+    return L.rlscan_gae(r, v, te, tr, bv, lv, adv, ret, E, T, 0.99, 0.95, ws, nws, N)
+
+
+def test_gae_validation(L):
+    assert gae(L, r=N) == NULL_ARG
+    assert b"rewards" in L.rlscan_last_error()
+    assert gae(L, v=N) == NULL_ARG
+    assert gae(L, te=N) == NULL_ARG
+    assert gae(L, adv=N) == NULL_ARG
+    assert gae(L, E=0) == BAD_SHAPE
+    assert gae(L, T=0) == BAD_SHAPE
+    assert gae(L, E=-3) == BAD_SHAPE
+    assert gae(L, E=1 << 45, T=1 << 20) == BAD_SHAPE
+    assert gae(L, lv=P, bv=P) == CONFLICT
+    assert gae(L, lv=P, tr=P) == CONFLICT
+    assert L.rlscan_gae(P, P, P, N, N, N, P, N, 4, 8, float("nan"), 0.95, N, 0, N) == BAD_PARAM
+
+
+def test_lookback_shapes_require_workspace(L):
+    # T = 1000 does not divide a 1024-element tile: rows straddle tiles
+    assert gae(L, E=4096, T=1000) == WORKSPACE
+    assert b"workspace" in L.rlscan_last_error()
+    # too small
+    assert gae(L, E=4096, T=1000, ws=ctypes.c_void_p(0x100000), nws=300) == WORKSPACE
+    # misaligned
+    need = L.rlscan_workspace_bytes(4096, 1000)
+    assert gae(L, E=4096, T=1000, ws=ctypes.c_void_p(0x100010), nws=need) == WORKSPACE
+    # long rows
+    assert L.rlscan_returns(P, N, P, N, N, P, 64, 131072, 0.999, 1.0, N, 0, N) == WORKSPACE
+    assert L.rlscan_prefix(P, P, N, P, 64, 131072, 1.0, 0, N, 0, N) == WORKSPACE
+
+
+def test_vtrace_validation(L):
+    def call(lpt=P, lpb=N, v=P, r=P, te=P, tr=N, bv=N, lv=N, vs=P, pg=N, E=4, T=8, rb=1.0, cb=1.0):
+        return L.rlscan_vtrace(lpt, lpb, v, r, te, tr, bv, lv, vs, pg, E, T, 0.99, rb, cb, N, 0, N)
+    assert call(lpt=N) == NULL_ARG
+    assert call(v=N) == NULL_ARG
+    assert call(r=N) == NULL_ARG
+    assert call(te=N) == NULL_ARG
+    assert call(vs=N) == NULL_ARG
+    assert call(T=0) == BAD_SHAPE
+    assert call(lv=P, bv=P) == CONFLICT
+    assert call(rb=float("nan")) == BAD_PARAM
+
+
+def test_retrace_validation(L):
+    def call(pi=P, mu=P, q=P, qn=P, act=P, r=P, te=P, tr=N, qr=P, adv=N, E=4, T=8, A=18):
+        return L.rlscan_retrace(pi, mu, q, qn, act, r, te, tr, qr, adv, E, T, A,
+                                0.99, 0.95, 1.0, 1.0, N, 0, N)
+    for kw in ("pi", "mu", "q", "qn", "act", "r", "te", "qr"):
+        assert call(**{kw: N}) == NULL_ARG, kw
+    assert call(A=0) == BAD_SHAPE
+    assert call(A=129) == BAD_SHAPE
+    assert call(E=0) == BAD_SHAPE
+
+
+def test_returns_and_prefix_validation(L):
+    assert L.rlscan_returns(N, N, P, N, N, P, 4, 8, 0.99, 0.9, N, 0, N) == NULL_ARG
+    assert L.rlscan_returns(P, N, N, N, N, P, 4, 8, 0.99, 0.9, N, 0, N) == NULL_ARG
+    assert L.rlscan_returns(P, N, P, N, N, N, 4, 8, 0.99, 0.9, N, 0, N) == NULL_ARG
+    assert L.rlscan_returns(P, N, P, N, N, P, 4, 0, 0.99, 0.9, N, 0, N) == BAD_SHAPE
+    assert L.rlscan_prefix(N, P, N, P, 4, 8, 1.0, 0, N, 0, N) == NULL_ARG
+    assert L.rlscan_prefix(P, N, N, P, 4, 8, 1.0, 0, N, 0, N) == NULL_ARG
+    assert L.rlscan_prefix(P, P, N, N, 4, 8, 1.0, 0, N, 0, N) == NULL_ARG
+    assert L.rlscan_prefix(P, P, N, P, 4, 8, 1.0, 7, N, 0, N) == BAD_PARAM
+    assert L.rlscan_prefix(P, P, N, P, 4, 8, float("nan"), 0, N, 0, N) == BAD_PARAM
+
+
+def test_workspace_init_validation(L):
+    assert L.rlscan_workspace_init(N, 4096, N) == NULL_ARG
+    assert L.rlscan_workspace_init(ctypes.c_void_p(0x1010), 4096, N) == WORKSPACE
+    assert L.rlscan_workspace_init(ctypes.c_void_p(0x1000), 100, N) == WORKSPACE
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(2, 8)
+    with pytest.raises(ValueError, match="GPU"):
+        ops.gae(x, x, x)
+    with pytest.raises(TypeError, match="float32"):
+        ops.gae(x.double(), x, x)
+    with pytest.raises(ValueError, match="boundary"):
+        ops._forward(x, x, None, 1.0, "middle")

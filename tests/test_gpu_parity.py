@@ -1,0 +1,438 @@
+"""GPU parity: every estimator through the C ABI (ctypes binding) against the
+float64 oracle on the same seeded fp32 inputs.
+
+Tolerance: max |gpu - oracle| <= tol * max(1, |oracle|) elementwise with
+tol = 1e-4 for T <= 4096 and 1e-3 for T up to 131072.  Integer-valued work
+(the prefix sum of ones) and the 0/1 boundary masking are checked bit-exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import golden_cases
+import oracle
+from linear_recurrence_scan_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def tol_for(T):
+    return 1e-4 if T <= 4096 else 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible AMD GPU"
+    assert ops.lib() is not None  # fails loudly if librlscan.so is missing
+    yield
+    assert ops.workspace_error() == 0, "a look-back wait exceeded its bound"
+
+
+def dev(x, dtype=None):
+    if x is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to("cuda")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def assert_close(got, want, T, what=""):
+    g = host(got) if isinstance(got, torch.Tensor) else got
+    err = np.abs(g - want) / np.maximum(1.0, np.abs(want))
+    worst = np.unravel_index(np.argmax(err), err.shape)
+    assert err.max() <= tol_for(T), (
+        f"{what}: max rel err {err.max():.3e} at {worst}: gpu {g[worst]!r} oracle {want[worst]!r}")
+
+
+f32 = np.float32
+
+
+# ---------------------------------------------------------------------------
+# the wave-scan primitive on its own
+# ---------------------------------------------------------------------------
+
+def test_wave_scan_primitive_layout():
+    rng = np.random.default_rng(0)
+    n = 8
+    a = rng.standard_normal(64 * n).astype(f32)
+    b = (rng.random(64 * n) * 1.5).astype(f32)
+    b[::7] = 0.0
+    oa = torch.empty(64 * n, device="cuda")
+    ob = torch.empty(64 * n, device="cuda")
+    ops.rlscan_debug_wave_scan(dev(a), dev(b), oa, ob)
+    wa = np.empty(64 * n)
+    wb = np.empty(64 * n)
+    for w in range(n):
+        acc_a, acc_b = 0.0, 1.0
+        for l in range(64):
+            i = 64 * w + l
+            acc_a = float(a[i]) + float(b[i]) * acc_a
+            acc_b = float(b[i]) * acc_b
+            wa[i], wb[i] = acc_a, acc_b
+    np.testing.assert_allclose(host(oa), wa, rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(host(ob), wb, rtol=1e-5, atol=1e-30)
+
+
+# ---------------------------------------------------------------------------
+# hand-worked golden examples (exact dyadic values)
+# ---------------------------------------------------------------------------
+
+def run_gpu_case(case):
+    a = golden_cases.arrays(case)
+    p = case["params"]
+    est = case["estimator"]
+    g = {k: dev(v) for k, v in a.items()}
+    if est == "gae":
+        adv, ret = ops.gae(g["rewards"], g["values"], g["terminateds"], g.get("truncateds"),
+                           p["gamma"], p["lambda"], g.get("bootstrap_values"), g.get("last_value"),
+                           want_returns=True)
+        return {"advantages": adv, "returns": ret}
+    if est == "vtrace":
+        vs, pg = ops.vtrace(g["log_rhos"], None, g["values"], g["rewards"], g["terminateds"],
+                            g.get("truncateds"), p["gamma"], p["rho_bar"], p["c_bar"],
+                            g.get("bootstrap_values"), g.get("last_value"))
+        return {"vs": vs, "pg_advantages": pg}
+    if est == "retrace":
+        q, adv = ops.retrace(g["pi_target"], g["mu_taken"], g["q_taken"], g["next_q_all"],
+                             g["actions"], g["rewards"], g["terminateds"], g.get("truncateds"),
+                             p["gamma"], p["lambda"], p["c_bar"], p["rho_bar"])
+        return {"q_ret": q, "advantages": adv}
+    if est == "discounted":
+        return {"returns": ops.discounted_returns(g["rewards"], g["terminateds"], g.get("truncateds"),
+                                                  p["gamma"], g.get("bootstrap_values"))}
+    if est == "lambda_returns":
+        return {"returns": ops.lambda_returns(g["rewards"], g["next_values"], g["terminateds"],
+                                              g.get("truncateds"), p["gamma"], p["lambda"],
+                                              g.get("bootstrap_values"))}
+    if est == "prefix":
+        return {b: ops.episodic_prefix_sum(g["inputs"], g["dones"], g.get("seed_values"), b)
+                for b in ("ends_at", "starts_at")}
+    if est == "traces":
+        x = g["inputs"]
+        out = torch.empty_like(x)
+        ops.rlscan_prefix(x, g["dones"], g.get("seed_values"), out, p["decay"], "ends_at")
+        return {"traces": out}
+    raise KeyError(est)
+
+
+@pytest.mark.parametrize("case", golden_cases.load(), ids=lambda c: c["id"])
+def test_hand_examples(case):
+    got = run_gpu_case(case)
+    for key, want in case["expected"].items():
+        w = np.asarray(want, np.float64)
+        g = host(got[key])
+        assert np.max(np.abs(g - w) / np.maximum(1, np.abs(w))) <= 1e-6, (key, g, w)
+
+
+# ---------------------------------------------------------------------------
+# GAE
+# ---------------------------------------------------------------------------
+
+GAE_SHAPES = [
+    (8, 128, "last"),        # the 8 x 128 workload
+    (512, 1024, "2d"),       # the 4096 x 1024 recipe at 1/8 of the rows
+    (37, 1000, "2d"),        # rows straddle tiles: look-back across rows
+    (13, 333, "last"),
+    (5, 1, "2d"), (7, 2, "last"), (9, 3, "2d"), (11, 5, None),
+    (3, 4099, "2d"),         # one row spans several 4096-element tiles plus a tail
+    (2, 8191, "last"),
+    (1, 20000, "2d"),
+    (300, 257, "2d"),
+]
+
+
+@pytest.mark.parametrize("E,T,boot", GAE_SHAPES)
+def test_gae_parity(E, T, boot):
+    trunc = boot == "2d"
+    d = synth.gae_inputs(E, T, seed=7 + E * 131 + T, p_term=0.02, p_trunc=0.01 if trunc else 0.0,
+                         truncations=trunc, boot=boot)
+    want_adv, want_ret = oracle.gae(d["rewards"], d["values"], d["terminateds"], d["truncateds"],
+                                    f32(0.99), f32(0.95), d["bootstrap_values"], d["last_value"])
+    adv, ret = ops.gae(dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]),
+                       dev(d["truncateds"]), 0.99, 0.95, dev(d["bootstrap_values"]),
+                       dev(d["last_value"]), want_returns=True)
+    assert_close(adv, want_adv, T, "advantages")
+    assert_close(ret, want_ret, T, "returns")
+
+
+def test_gae_without_truncations_reads_only_last_bootstrap_column():
+    E, T = 64, 777
+    d = synth.gae_inputs(E, T, seed=3, truncations=False, boot=None)
+    stray = np.random.default_rng(1).standard_normal((E, T)).astype(f32)
+    want, _ = oracle.gae(d["rewards"], d["values"], d["terminateds"], None, f32(0.97), f32(0.9),
+                         stray, None)
+    adv = ops.gae(dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]), None, 0.97, 0.9,
+                  dev(stray))
+    assert_close(adv, want, T, "advantages")
+
+
+def test_gae_unaligned_pointers():
+    """Views that start 4 bytes into an allocation take the scalar-load path."""
+    E, T = 33, 515
+    d = synth.gae_trunc(E=E, T=T, seed=11)
+
+    def shifted(x):
+        buf = torch.empty(E * T + 1, device="cuda")
+        buf[1:] = dev(x).reshape(-1)
+        return buf[1:].view(E, T)
+
+    want_adv, want_ret = oracle.gae(d["rewards"], d["values"], d["terminateds"], d["truncateds"],
+                                    f32(0.99), f32(0.95), d["bootstrap_values"])
+    adv = shifted(np.zeros((E, T), f32))
+    ret = shifted(np.zeros((E, T), f32))
+    ops.rlscan_gae(shifted(d["rewards"]), shifted(d["values"]), shifted(d["terminateds"]),
+                   shifted(d["truncateds"]), shifted(d["bootstrap_values"]), None, adv, ret,
+                   0.99, 0.95)
+    assert_close(adv, want_adv, T, "advantages")
+    assert_close(ret, want_ret, T, "returns")
+
+
+def test_gae_full_size_workload():
+    """The 4096 x 1024 workload with truncations, in the launch configuration the
+    benchmark times, checked on every element."""
+    d = synth.gae_trunc()
+    want_adv, want_ret = oracle.gae(d["rewards"], d["values"], d["terminateds"], d["truncateds"],
+                                    f32(0.99), f32(0.95), d["bootstrap_values"])
+    adv, ret = ops.gae(dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]),
+                       dev(d["truncateds"]), 0.99, 0.95, dev(d["bootstrap_values"]),
+                       want_returns=True)
+    assert_close(adv, want_adv, 1024, "advantages")
+    assert_close(ret, want_ret, 1024, "returns")
+
+
+# ---------------------------------------------------------------------------
+# V-trace
+# ---------------------------------------------------------------------------
+
+VTRACE_CASES = [
+    (16, 4096, False, 0.0, "last", (1.0, 1.0)),
+    (9, 1500, True, 0.01, "2d", (1.0, 1.0)),
+    (7, 999, True, 0.01, "trunc_last", (0.8, 1.2)),
+    (40, 100, False, 0.0, None, (2.0, 0.5)),
+    (2, 9000, False, 0.0, "last", (1.0, 1.0)),
+]
+
+
+@pytest.mark.parametrize("E,T,two,p_trunc,boot,clips", VTRACE_CASES)
+def test_vtrace_parity(E, T, two, p_trunc, boot, clips):
+    b = "last" if boot == "trunc_last" else boot
+    d = synth.vtrace_inputs(E, T, seed=E * 7 + T, p_trunc=p_trunc, two_logprobs=two, boot=b)
+    rho_bar, c_bar = clips
+    want_vs, want_pg = oracle.vtrace(d["log_pi_target"], d["log_pi_behavior"], d["values"],
+                                     d["rewards"], d["terminateds"], d["truncateds"], f32(0.99),
+                                     f32(rho_bar), f32(c_bar), d["bootstrap_values"], d["last_value"])
+    vs, pg = ops.vtrace(dev(d["log_pi_target"]), dev(d["log_pi_behavior"]), dev(d["values"]),
+                        dev(d["rewards"]), dev(d["terminateds"]), dev(d["truncateds"]), 0.99,
+                        rho_bar, c_bar, dev(d["bootstrap_values"]), dev(d["last_value"]))
+    assert_close(vs, want_vs, T, "vs")
+    assert_close(pg, want_pg, T, "pg")
+
+
+def test_vtrace_full_size_workload():
+    d = synth.vtrace_inputs()
+    want_vs, want_pg = oracle.vtrace(d["log_pi_target"], None, d["values"], d["rewards"],
+                                     d["terminateds"], None, f32(0.99), 1.0, 1.0, None,
+                                     d["last_value"])
+    vs, pg = ops.vtrace(dev(d["log_pi_target"]), None, dev(d["values"]), dev(d["rewards"]),
+                        dev(d["terminateds"]), None, 0.99, 1.0, 1.0, None, dev(d["last_value"]))
+    assert_close(vs, want_vs, 4096, "vs")
+    assert_close(pg, want_pg, 4096, "pg")
+
+
+# ---------------------------------------------------------------------------
+# Retrace
+# ---------------------------------------------------------------------------
+
+RETRACE_CASES = [
+    (16, 2048, 18, 0.0),
+    (8, 500, 18, 0.01),
+    (5, 77, 1, 0.02),
+    (6, 300, 5, 0.02),
+    (4, 1030, 33, 0.01),
+    (3, 129, 128, 0.01),
+    (64, 64, 7, 0.05),
+]
+
+
+@pytest.mark.parametrize("E,T,A,p_trunc", RETRACE_CASES)
+def test_retrace_parity(E, T, A, p_trunc):
+    d = synth.retrace_inputs(E, T, A, seed=E + 3 * T + A, p_term=0.01, p_trunc=p_trunc)
+    args = (d["pi_target"], d["mu_taken"], d["q_taken"], d["next_q_all"], d["actions"],
+            d["rewards"], d["terminateds"], d["truncateds"])
+    want_q, want_adv = oracle.retrace(*args, f32(0.99), f32(0.95), 1.0, 1.0)
+    g = [dev(x) for x in args]
+    q, adv = ops.retrace(*g, 0.99, 0.95, 1.0, 1.0)
+    assert_close(q, want_q, T, "q_ret")
+    assert_close(adv, want_adv, T, "advantages")
+
+
+def test_retrace_full_size_workload():
+    d = synth.retrace_inputs()
+    args = (d["pi_target"], d["mu_taken"], d["q_taken"], d["next_q_all"], d["actions"],
+            d["rewards"], d["terminateds"], d["truncateds"])
+    want_q, want_adv = oracle.retrace(*args, f32(0.99), f32(0.95), 1.0, 1.0)
+    q, adv = ops.retrace(*[dev(x) for x in args], 0.99, 0.95, 1.0, 1.0)
+    assert_close(q, want_q, 2048, "q_ret")
+    assert_close(adv, want_adv, 2048, "advantages")
+
+
+# ---------------------------------------------------------------------------
+# TD(lambda) and discounted returns
+# ---------------------------------------------------------------------------
+
+RETURNS_CASES = [(8, 131072), (33, 1000), (4, 5000), (100, 64), (3, 3), (1, 70001)]
+
+
+@pytest.mark.parametrize("E,T", RETURNS_CASES)
+@pytest.mark.parametrize("kind", ["lambda", "discounted", "discounted_no_trunc"])
+def test_returns_parity(E, T, kind):
+    d = synth.returns_inputs(E, T, seed=E * 5 + T, p_term=0.003, p_trunc=0.002)
+    tr = None if kind == "discounted_no_trunc" else d["truncateds"]
+    if kind == "lambda":
+        want = oracle.lambda_returns(d["rewards"], d["next_values"], d["terminateds"], tr,
+                                     f32(0.999), f32(0.9), d["bootstrap_values"])
+        got = ops.lambda_returns(dev(d["rewards"]), dev(d["next_values"]), dev(d["terminateds"]),
+                                 dev(tr), 0.999, 0.9, dev(d["bootstrap_values"]))
+    else:
+        want = oracle.discounted_returns(d["rewards"], d["terminateds"], tr, f32(0.999),
+                                         d["bootstrap_values"])
+        got = ops.discounted_returns(dev(d["rewards"]), dev(d["terminateds"]), dev(tr), 0.999,
+                                     dev(d["bootstrap_values"]))
+    assert_close(got, want, T, kind)
+
+
+def test_discounted_full_size_workload():
+    d = synth.long_row_inputs()
+    want = oracle.discounted_returns(d["rewards"], d["terminateds"], d["truncateds"], f32(0.999),
+                                     d["bootstrap_values"])
+    got = ops.discounted_returns(dev(d["rewards"]), dev(d["terminateds"]), dev(d["truncateds"]),
+                                 0.999, dev(d["bootstrap_values"]))
+    assert_close(got, want, 131072, "discounted")
+
+
+# ---------------------------------------------------------------------------
+# forward scans
+# ---------------------------------------------------------------------------
+
+PREFIX_CASES = [(8, 131072), (50, 1000), (3, 4097), (100, 17), (7, 1), (2, 10000)]
+
+
+@pytest.mark.parametrize("E,T", PREFIX_CASES)
+@pytest.mark.parametrize("boundary", ["ends_at", "starts_at"])
+@pytest.mark.parametrize("decay", [1.0, 0.9405])
+def test_forward_parity(E, T, boundary, decay):
+    d = synth.forward_inputs(E, T, seed=E + T, p_done=0.003)
+    want = oracle.forward_scan(d["inputs"], d["dones"], d["seed_values"], f32(decay), boundary)
+    out = torch.empty((E, T), device="cuda")
+    ops.rlscan_prefix(dev(d["inputs"]), dev(d["dones"]), dev(d["seed_values"]), out, decay, boundary)
+    assert_close(out, want, T, f"{boundary} decay={decay}")
+
+
+def test_eligibility_traces_helper():
+    d = synth.forward_inputs(20, 3000, seed=4, p_done=0.01)
+    k = f32(0.99 * 0.95)
+    want = oracle.forward_scan(d["inputs"], d["dones"], d["seed_values"], k, "ends_at")
+    got = ops.eligibility_traces(dev(d["inputs"]), dev(d["dones"]), 0.99, 0.95, dev(d["seed_values"]))
+    assert_close(got, want, 3000, "traces")
+
+
+def test_prefix_sum_full_size_workload():
+    d = synth.long_row_inputs()
+    want = oracle.episodic_prefix_sum(d["rewards"], d["dones"], None, "ends_at")
+    got = ops.episodic_prefix_sum(dev(d["rewards"]), dev(d["dones"]))
+    assert_close(got, want, 131072, "prefix")
+
+
+def test_prefix_sum_of_ones_is_bit_exact():
+    """Counting steps in an episode is exact integer work in fp32 (< 2^24)."""
+    E, T = 16, 131072
+    rng = np.random.default_rng(12)
+    dones = (rng.random((E, T)) < 1e-4).astype(f32)
+    want = oracle.episodic_prefix_sum(np.ones((E, T), f32), dones, None, "ends_at")
+    got = ops.episodic_prefix_sum(torch.ones(E, T, device="cuda"), dev(dones))
+    np.testing.assert_array_equal(host(got), want)
+
+
+# ---------------------------------------------------------------------------
+# boundary masking is exact; results are reproducible
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("est", ["gae", "vtrace", "lambda", "prefix"])
+def test_inputs_after_done_do_not_reach_back_bit_exact(est):
+    E, T, t_d = 12, 3000, 1700
+    rng = np.random.default_rng(21)
+    d = synth.gae_inputs(E, T, seed=21, p_term=0.0, p_trunc=0.0, boot="2d")
+    term, trunc = d["terminateds"].copy(), d["truncateds"].copy()
+    term[: E // 2, t_d] = 1
+    trunc[E // 2:, t_d] = 1
+    boot = d["bootstrap_values"]
+    boot[E // 2:, t_d] = rng.standard_normal(E - E // 2)
+
+    def pert(x):
+        y = x.copy()
+        y[:, t_d + 1:] = rng.standard_normal(y[:, t_d + 1:].shape)
+        return y.astype(f32)
+
+    def run(r, v, bt):
+        if est == "gae":
+            return [ops.gae(dev(r), dev(v), dev(term), dev(trunc), 0.99, 0.95, dev(bt))]
+        if est == "vtrace":
+            lr = np.sin(np.arange(E * T, dtype=f32)).reshape(E, T) * 0.5
+            return list(ops.vtrace(dev(lr), None, dev(v), dev(r), dev(term), dev(trunc), 0.99,
+                                   1.0, 1.0, dev(bt)))
+        if est == "lambda":
+            return [ops.lambda_returns(dev(r), dev(v), dev(term), dev(trunc), 0.99, 0.9, dev(bt))]
+        # forward: inputs before a reset must not leak past it
+        dn = np.maximum(term, trunc)
+        return [ops.episodic_prefix_sum(dev(r), dev(dn), None, "ends_at")]
+
+    base = [host(x) for x in run(d["rewards"], d["values"], boot)]
+    if est == "prefix":
+        # forward direction: perturb everything at or before t_d, compare after it
+        r2 = d["rewards"].copy()
+        r2[:, : t_d + 1] = rng.standard_normal((E, t_d + 1))
+        pert_out = [host(x) for x in run(r2, d["values"], boot)]
+        for a, b in zip(base, pert_out):
+            np.testing.assert_array_equal(a[:, t_d + 1:], b[:, t_d + 1:])
+        return
+    pert_out = [host(x) for x in run(pert(d["rewards"]), pert(d["values"]), pert(boot))]
+    for a, b in zip(base, pert_out):
+        np.testing.assert_array_equal(a[:, : t_d + 1], b[:, : t_d + 1])
+
+
+@pytest.mark.parametrize("shape", [(37, 1000), (8, 131072), (3, 4099)])
+def test_lookback_results_are_bitwise_reproducible(shape):
+    E, T = shape
+    d = synth.returns_inputs(E, T, seed=99, p_term=0.0005, p_trunc=0.0005)
+    args = [dev(d[k]) for k in ("rewards", "next_values", "terminateds", "truncateds",
+                                "bootstrap_values")]
+    first = host(ops.lambda_returns(*args[:4], 0.999, 0.97, args[4]))
+    for _ in range(4):
+        again = host(ops.lambda_returns(*args[:4], 0.999, 0.97, args[4]))
+        np.testing.assert_array_equal(first, again)
+
+
+def test_calls_on_one_stream_share_a_workspace_without_clearing():
+    """Consecutive look-back calls of different estimators on one stream, with no
+    synchronisation in between, each see a clean workspace."""
+    E, T = 9, 5000
+    d = synth.returns_inputs(E, T, seed=5)
+    f = synth.forward_inputs(E, T, seed=6)
+    want_r = oracle.discounted_returns(d["rewards"], d["terminateds"], d["truncateds"], f32(0.99),
+                                       d["bootstrap_values"])
+    want_f = oracle.forward_scan(f["inputs"], f["dones"], f["seed_values"], 1.0, "ends_at")
+    outs = []
+    for _ in range(3):
+        outs.append(ops.discounted_returns(dev(d["rewards"]), dev(d["terminateds"]),
+                                           dev(d["truncateds"]), 0.99, dev(d["bootstrap_values"])))
+        outs.append(ops.episodic_prefix_sum(dev(f["inputs"]), dev(f["dones"]), dev(f["seed_values"])))
+    for i, o in enumerate(outs):
+        assert_close(o, want_r if i % 2 == 0 else want_f, T, f"call {i}")
