@@ -106,7 +106,8 @@ rlscan_status rlscan_workspace_error(const void* ws, uint32_t* error_out, rlscan
  *         and column T-1 by contract), without truncateds only column T-1 is
  *         read.  last_value: [E] or NULL, fills column T-1 (B_{T-1}).
  * Outputs advantages [E,T]; returns [E,T] or NULL to skip.
- * Errors  NULL required pointer -> NULL_ARG; E < 1 or T < 1 -> BAD_SHAPE;
+ * Errors  NULL required pointer -> NULL_ARG; E < 1, T < 1, T >= 2^31 or
+ *         E*T >= 2^46 -> BAD_SHAPE;
  *         last_value together with bootstrap_values or truncateds -> CONFLICT.
  */
 rlscan_status rlscan_gae(const float* rewards, const float* values, const float* terminateds,

@@ -25,20 +25,21 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: install ROCm or set HIPCC")
 
 
-def command(out: str) -> list[str]:
+def command(out: str, defines=()) -> list[str]:
     return [
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-Wall", "-Wno-unused-parameter",
         # packed fp32 VALU forms stay disabled in every HIP translation unit
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        *[f"-D{d}" for d in defines],
         "-x", "hip", *[os.path.join(CSRC, s) for s in SOURCES],
         "-o", out,
     ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = command(tmp)
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = command(tmp, defines)
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,8 +47,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr[-6000:]}")
     if verbose and proc.stderr.strip():
         print(proc.stderr[-3000:], file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

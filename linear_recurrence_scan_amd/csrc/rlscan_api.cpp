@@ -16,15 +16,27 @@ thread_local char g_last_error[512] = "";
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Tile size override for tuning experiments: RLSCAN_TILE=256|1024|4096.
-int tile_override() {
-    static int cached = -1;
-    if (cached < 0) {
-        const char* s = std::getenv("RLSCAN_TILE");
-        int v = s ? std::atoi(s) : 0;
-        cached = (v == 256 || v == 1024 || v == 4096) ? v : 0;
+// Launch-shape override for tuning experiments: RLSCAN_CFG="tile,waves" with
+// one of 256,1 / 1024,1 / 2048,4 / 4096,4 / 4096,8.
+bool cfg_override(int& tile, int& waves) {
+    static int cached_tile = -1, cached_waves = 0;
+    if (cached_tile < 0) {
+        cached_tile = 0;
+        const char* s = std::getenv("RLSCAN_CFG");
+        int t = 0, w = 0;
+        if (s && std::sscanf(s, "%d,%d", &t, &w) == 2) {
+            const bool ok = (t == 256 && w == 1) || (t == 1024 && w == 1) || (t == 2048 && w == 4) ||
+                            (t == 4096 && w == 4) || (t == 4096 && w == 8);
+            if (ok) {
+                cached_tile = t;
+                cached_waves = w;
+            }
+        }
     }
-    return cached;
+    if (cached_tile == 0) return false;
+    tile = cached_tile;
+    waves = cached_waves;
+    return true;
 }
 
 constexpr int64_t kMaxTiles = (int64_t)1 << 31;
@@ -37,16 +49,28 @@ size_t ws_bytes_for_tiles(int64_t tiles) {
 // Plans a launch of a 4-elements-per-lane kernel.
 rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
     const int64_t N = E * T;
-    int tile = tile_override();
-    if (tile == 0) {
-        if (T >= 4096) tile = 4096;
-        else if (N <= (int64_t)256 * 1024) tile = 256;
-        else tile = 1024;
+    int tile = 0, waves = 0;
+    if (!cfg_override(tile, waves)) {
+        // Measured on MI355X (4096 x 1024 GAE): 4 waves x 2 segments per
+        // workgroup is fastest for rows of a few thousand steps; rows of 4096
+        // steps or longer take 4096-element tiles (whole rows per tile, or
+        // fewer look-back hops along a long row); tiny problems take small
+        // tiles so that more workgroups share the work.
+        if (N <= (int64_t)256 * 1024) {
+            tile = 256;
+            waves = 1;
+        } else if (T >= 4096) {
+            tile = 4096;
+            waves = 4;
+        } else {
+            tile = 2048;
+            waves = 4;
+        }
     }
     plan.tile = tile;
-    plan.waves = tile == 4096 ? 4 : 1;
+    plan.waves = waves;
     plan.geo.N = N;
-    plan.geo.T = T;
+    plan.geo.T = (uint32_t)T;
     plan.geo.num_tiles = (N + tile - 1) / tile;
     plan.geo.magic = T < tile ? (uint32_t)(0xFFFFFFFFu / (uint32_t)T) : 0u;
     plan.geo.vec_ok = vec_ok ? 1 : 0;
@@ -66,7 +90,7 @@ rlscan_status plan_retrace(int64_t E, int64_t T, int64_t A, Plan& plan, bool vec
     plan.tile = tile;
     plan.waves = waves;
     plan.geo.N = N;
-    plan.geo.T = T;
+    plan.geo.T = (uint32_t)T;
     plan.geo.num_tiles = (N + tile - 1) / tile;
     plan.geo.magic = T < tile ? (uint32_t)(0xFFFFFFFFu / (uint32_t)T) : 0u;
     plan.geo.vec_ok = vec_ok ? 1 : 0;
@@ -77,7 +101,8 @@ rlscan_status plan_retrace(int64_t E, int64_t T, int64_t A, Plan& plan, bool vec
 
 rlscan_status check_shape(int64_t E, int64_t T) {
     if (E < 1 || T < 1) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs and seq_len must be >= 1");
-    if (T > ((int64_t)1 << 40) || E > ((int64_t)1 << 40) || E > (((int64_t)1 << 46) / T))
+    if (T >= ((int64_t)1 << 31)) return set_error(RLSCAN_ERR_BAD_SHAPE, "seq_len must be < 2^31");
+    if (E > ((int64_t)1 << 40) || E > (((int64_t)1 << 46) / T))
         return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
     return RLSCAN_OK;
 }

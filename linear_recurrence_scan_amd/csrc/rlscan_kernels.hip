@@ -1,10 +1,15 @@
 // rlscan_kernels.hip -- fused estimator kernels for gfx950.
 //
-// One templated kernel (scan_kernel) runs every estimator: the estimator's
-// prologue reads its raw inputs once and builds (alpha_t, beta_t) in
-// registers, the shared affine scan resolves the recurrence, and the
-// estimator's epilogue writes its outputs from the scanned values.  Nothing is
-// materialised in HBM between those steps (rl-triton paper, Sec. 4.2, Table 2).
+// One templated kernel (scan_kernel) runs every estimator in three phases:
+//   1. load:   every input of every segment the wave owns is requested before
+//              any arithmetic, so a wave keeps all its reads in flight at once;
+//   2. coeffs: the estimator builds (alpha_t, beta_t) in registers from the
+//              raw inputs, and the shared affine scan resolves the recurrence
+//              (lane fold, DPP wave scan, LDS across waves, look-back across
+//              workgroups);
+//   3. epilogue: the estimator writes its outputs from the scanned values.
+// Nothing is materialised in HBM between those steps (rl-triton paper,
+// Sec. 4.2, Table 2).
 //
 // Row boundaries are handled by folding the row's boundary carry into alpha
 // and setting beta = 0 at the row's first scan element (paper, Sec. 3.2 and
@@ -24,6 +29,14 @@ struct SegInfo {
     float* lds;         // this wave's dynamic LDS (Retrace only)
 };
 
+// Continuation value at a row end when it does not come from a full
+// [E,T] bootstrap array read alongside the other inputs: last_value[row], or
+// column T-1 of bootstrap_values when there are no truncations.
+__device__ __forceinline__ float edge_bootstrap(const float* last_value, const float* boot,
+                                                int64_t row, int64_t flat) {
+    return last_value ? last_value[row] : boot[flat];
+}
+
 // ---------------------------------------------------------------------------
 // GAE (kernels page, compute_gae Recurrence; paper Sec. 3.3.1, Table 1)
 // ---------------------------------------------------------------------------
@@ -31,50 +44,67 @@ struct GaeOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = true;
     GaeArgs p;
+    struct Raw {
+        float R[G], V[G], TE[G], TR[G], B[G];  // B: continuation value (0 where none)
+        float halo;
+    };
     struct Keep {
         float v;
     };
+    __device__ size_t lds_floats_per_wave() const { return 0; }
 
-    __device__ void prologue(const Geo& g, const SegInfo& si, const Slots<G>& s, float (&al)[G],
-                             float (&be)[G], Keep (&kp)[G]) const {
-        float R[G], V[G], TE[G], TR[G] = {0.f, 0.f, 0.f, 0.f}, B[G] = {0.f, 0.f, 0.f, 0.f};
-        load_group<G, true>(p.rewards, g, s, R);
-        load_group<G, true>(p.values, g, s, V);
-        load_group<G, true>(p.terminateds, g, s, TE);
+    template <bool FAST>
+    __device__ void load(const Geo& g, const Tile& tl, const SegInfo& si, const Grp& gr,
+                         Raw& w) const {
+        load_group<G, true, FAST>(p.rewards + tl.lo, gr, w.R);
+        load_group<G, true, FAST>(p.values + tl.lo, gr, w.V);
+        load_group<G, true, FAST>(p.terminateds + tl.lo, gr, w.TE);
+#pragma unroll
+        for (int j = 0; j < G; ++j) w.TR[j] = w.B[j] = 0.f;
         if (p.truncateds) {
-            load_group<G, true>(p.truncateds, g, s, TR);
-            if (p.bootstrap_values) load_group<G, true>(p.bootstrap_values, g, s, B);
+            load_group<G, true, FAST>(p.truncateds + tl.lo, gr, w.TR);
+            if (p.bootstrap_values) load_group<G, true, FAST>(p.bootstrap_values + tl.lo, gr, w.B);
+        } else if ((p.last_value || p.bootstrap_values) && (gr.edges & gr.valid)) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                if (bit(gr.edges & gr.valid, j)) {
+                    const uint32_t o = gr.off + flat_of_slot<G, true>(j);
+                    w.B[j] = edge_bootstrap(p.last_value, p.bootstrap_values, row_at(g, tl, o),
+                                            tl.lo + o);
+                }
         }
-        const float halo = (lane_id() == 0 && si.halo_valid) ? p.values[si.halo_flat] : 0.f;
+        w.halo = (lane_id() == 0 && si.halo_valid) ? p.values[si.halo_flat] : 0.f;
+    }
+
+    __device__ void coeffs(const Grp& gr, const Raw& w, float (&al)[G], float (&be)[G],
+                           Keep (&kp)[G]) const {
         float VN[G];
-        scan_prev<G>(V, halo, VN);
+        scan_prev<G>(w.V, w.halo, VN);
         const float gl = p.gamma * p.lambda;
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            float b = B[j];
-            if (s.edge[j] && s.valid[j]) {
-                if (p.last_value) b = p.last_value[s.row[j]];
-                else if (!p.truncateds && p.bootstrap_values) b = p.bootstrap_values[s.flat[j]];
-            }
+            const bool edge = bit(gr.edges, j);
+            const float b = w.B[j];
             // successor value: bootstrap at the row end, else (1-trunc) V_{t+1} + B_t
-            const float vnext = s.edge[j] ? b : fmaf(1.f - TR[j], VN[j], b);
-            const float done = fminf(TE[j] + TR[j], 1.f);
-            const float a = fmaf(p.gamma * (1.f - TE[j]), vnext, R[j]) - V[j];
-            const float bb = s.edge[j] ? 0.f : gl * (1.f - done);  // A_T = 0
-            al[j] = s.valid[j] ? a : 0.f;
-            be[j] = s.valid[j] ? bb : 1.f;
-            kp[j].v = V[j];
+            const float vnext = edge ? b : fmaf(1.f - w.TR[j], VN[j], b);
+            const float done = fminf(w.TE[j] + w.TR[j], 1.f);
+            const float a = fmaf(p.gamma * (1.f - w.TE[j]), vnext, w.R[j]) - w.V[j];
+            const float bb = edge ? 0.f : gl * (1.f - done);  // A_T = 0
+            al[j] = bit(gr.valid, j) ? a : 0.f;
+            be[j] = bit(gr.valid, j) ? bb : 1.f;
+            kp[j].v = w.V[j];
         }
     }
 
-    __device__ void epilogue(const Geo& g, const Slots<G>& s, const float (&A)[G],
-                             const float (&)[G], const float (&)[G], const Keep (&kp)[G]) const {
-        store_group<G, true>(p.advantages, g, s, A);
+    template <bool FAST>
+    __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
+                             const float (&)[G], const Keep (&kp)[G]) const {
+        store_group<G, true, FAST>(p.advantages + tl.lo, gr, A);
         if (p.returns) {
             float R[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) R[j] = A[j] + kp[j].v;
-            store_group<G, true>(p.returns, g, s, R);
+            store_group<G, true, FAST>(p.returns + tl.lo, gr, R);
         }
     }
 };
@@ -91,58 +121,77 @@ struct VtraceOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = true;
     VtraceArgs p;
+    struct Raw {
+        float LP[G], LB[G], R[G], V[G], TE[G], TR[G], B[G];  // B: continuation value
+        float halo;
+    };
     struct Keep {
         float v, k;
     };
+    __device__ size_t lds_floats_per_wave() const { return 0; }
 
-    __device__ void prologue(const Geo& g, const SegInfo& si, const Slots<G>& s, float (&al)[G],
-                             float (&be)[G], Keep (&kp)[G]) const {
-        float LP[G], LB[G] = {0.f, 0.f, 0.f, 0.f}, R[G], V[G], TE[G];
-        float TR[G] = {0.f, 0.f, 0.f, 0.f}, B[G] = {0.f, 0.f, 0.f, 0.f};
-        load_group<G, true>(p.log_pi_target, g, s, LP);
-        if (p.log_pi_behavior) load_group<G, true>(p.log_pi_behavior, g, s, LB);
-        load_group<G, true>(p.values, g, s, V);
-        load_group<G, true>(p.rewards, g, s, R);
-        load_group<G, true>(p.terminateds, g, s, TE);
-        if (p.truncateds) {
-            load_group<G, true>(p.truncateds, g, s, TR);
-            if (p.bootstrap_values) load_group<G, true>(p.bootstrap_values, g, s, B);
+    template <bool FAST>
+    __device__ void load(const Geo& g, const Tile& tl, const SegInfo& si, const Grp& gr,
+                         Raw& w) const {
+        load_group<G, true, FAST>(p.log_pi_target + tl.lo, gr, w.LP);
+#pragma unroll
+        for (int j = 0; j < G; ++j) w.LB[j] = w.TR[j] = w.B[j] = 0.f;
+        if (p.log_pi_behavior) load_group<G, true, FAST>(p.log_pi_behavior + tl.lo, gr, w.LB);
+        load_group<G, true, FAST>(p.values + tl.lo, gr, w.V);
+        load_group<G, true, FAST>(p.rewards + tl.lo, gr, w.R);
+        load_group<G, true, FAST>(p.terminateds + tl.lo, gr, w.TE);
+        if (p.truncateds) load_group<G, true, FAST>(p.truncateds + tl.lo, gr, w.TR);
+        if (p.truncateds && p.bootstrap_values) {
+            load_group<G, true, FAST>(p.bootstrap_values + tl.lo, gr, w.B);
+        } else if ((p.last_value || p.bootstrap_values) && (gr.edges & gr.valid)) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                if (bit(gr.edges & gr.valid, j)) {
+                    const uint32_t o = gr.off + flat_of_slot<G, true>(j);
+                    w.B[j] = edge_bootstrap(p.last_value, p.bootstrap_values, row_at(g, tl, o),
+                                            tl.lo + o);
+                }
         }
-        const float halo = (lane_id() == 0 && si.halo_valid) ? p.values[si.halo_flat] : 0.f;
+        w.halo = (lane_id() == 0 && si.halo_valid) ? p.values[si.halo_flat] : 0.f;
+    }
+
+    __device__ void coeffs(const Grp& gr, const Raw& w, float (&al)[G], float (&be)[G],
+                           Keep (&kp)[G]) const {
         float VN[G];
-        scan_prev<G>(V, halo, VN);
+        scan_prev<G>(w.V, w.halo, VN);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            float b = B[j];
-            if (s.edge[j] && s.valid[j]) {
-                if (p.last_value) b = p.last_value[s.row[j]];
-                else if (!p.truncateds && p.bootstrap_values) b = p.bootstrap_values[s.flat[j]];
-            }
-            const float ratio = expf(LP[j] - LB[j]);
+            const bool edge = bit(gr.edges, j);
+            // with truncations B is the full array; without, only row ends hold
+            // their continuation value
+            const float b = w.B[j];
+            const float ratio = expf(w.LP[j] - w.LB[j]);
             const float rho = fminf(p.rho_bar, ratio);
             const float c = fminf(p.c_bar, ratio);
-            const float vnext = s.edge[j] ? b : fmaf(1.f - TR[j], VN[j], b);
-            const float done = fminf(TE[j] + TR[j], 1.f);
-            const float a = rho * (fmaf(p.gamma * (1.f - TE[j]), vnext, R[j]) - V[j]);
-            const float bb = s.edge[j] ? 0.f : p.gamma * c * (1.f - done);
-            al[j] = s.valid[j] ? a : 0.f;
-            be[j] = s.valid[j] ? bb : 1.f;
-            kp[j].v = V[j];
-            kp[j].k = s.edge[j] ? 0.f : p.gamma * rho * ((1.f - TE[j]) * (1.f - TR[j]));
+            const float vnext = edge ? b : fmaf(1.f - w.TR[j], VN[j], b);
+            const float done = fminf(w.TE[j] + w.TR[j], 1.f);
+            const float a = rho * (fmaf(p.gamma * (1.f - w.TE[j]), vnext, w.R[j]) - w.V[j]);
+            const float bb = edge ? 0.f : p.gamma * c * (1.f - done);
+            al[j] = bit(gr.valid, j) ? a : 0.f;
+            be[j] = bit(gr.valid, j) ? bb : 1.f;
+            kp[j].v = w.V[j];
+            kp[j].k = edge ? 0.f : p.gamma * rho * ((1.f - w.TE[j]) * (1.f - w.TR[j]));
         }
     }
 
-    __device__ void epilogue(const Geo& g, const Slots<G>& s, const float (&A)[G],
-                             const float (&prevA)[G], const float (&al)[G], const Keep (&kp)[G]) const {
+    template <bool FAST>
+    __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G],
+                             const float (&prevA)[G], const float (&al)[G],
+                             const Keep (&kp)[G]) const {
         float VS[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) VS[j] = A[j] + kp[j].v;
-        store_group<G, true>(p.vs, g, s, VS);
+        store_group<G, true, FAST>(p.vs + tl.lo, gr, VS);
         if (p.pg_advantages) {
             float PG[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) PG[j] = fmaf(kp[j].k, prevA[j], al[j]);
-            store_group<G, true>(p.pg_advantages, g, s, PG);
+            store_group<G, true, FAST>(p.pg_advantages + tl.lo, gr, PG);
         }
     }
 };
@@ -156,43 +205,54 @@ struct ReturnsOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = true;
     ReturnsArgs p;
+    struct Raw {
+        float R[G], TE[G], TR[G], B[G], NV[G], EB[G];  // EB: row-end carry without truncations
+    };
     struct Keep {};
+    __device__ size_t lds_floats_per_wave() const { return 0; }
 
-    __device__ void prologue(const Geo& g, const SegInfo&, const Slots<G>& s, float (&al)[G],
-                             float (&be)[G], Keep (&)[G]) const {
-        float R[G], TE[G], TR[G] = {0.f, 0.f, 0.f, 0.f}, B[G] = {0.f, 0.f, 0.f, 0.f};
-        float NV[G] = {0.f, 0.f, 0.f, 0.f};
-        load_group<G, true>(p.rewards, g, s, R);
-        load_group<G, true>(p.terminateds, g, s, TE);
+    template <bool FAST>
+    __device__ void load(const Geo&, const Tile& tl, const SegInfo&, const Grp& gr, Raw& w) const {
+        load_group<G, true, FAST>(p.rewards + tl.lo, gr, w.R);
+        load_group<G, true, FAST>(p.terminateds + tl.lo, gr, w.TE);
+#pragma unroll
+        for (int j = 0; j < G; ++j) w.TR[j] = w.B[j] = w.NV[j] = w.EB[j] = 0.f;
         if (p.truncateds) {
-            load_group<G, true>(p.truncateds, g, s, TR);
-            if (p.bootstrap_values) load_group<G, true>(p.bootstrap_values, g, s, B);
+            load_group<G, true, FAST>(p.truncateds + tl.lo, gr, w.TR);
+            if (p.bootstrap_values) load_group<G, true, FAST>(p.bootstrap_values + tl.lo, gr, w.B);
+        } else if (p.bootstrap_values && (gr.edges & gr.valid)) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                if (bit(gr.edges & gr.valid, j))
+                    w.EB[j] = p.bootstrap_values[tl.lo + gr.off + flat_of_slot<G, true>(j)];
         }
-        if (p.next_values) load_group<G, true>(p.next_values, g, s, NV);
+        if (p.next_values) load_group<G, true, FAST>(p.next_values + tl.lo, gr, w.NV);
+    }
+
+    __device__ void coeffs(const Grp& gr, const Raw& w, float (&al)[G], float (&be)[G],
+                           Keep (&)[G]) const {
         const float lam = p.next_values ? p.lambda : 1.f;
         const float gl = p.gamma * lam;
         const float g1l = p.gamma * (1.f - lam);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            const float done = fminf(TE[j] + TR[j], 1.f);
-            float a = fmaf(p.gamma * TR[j], B[j], R[j]);
-            if (p.next_values) a = fmaf(g1l * (1.f - done), NV[j], a);
+            const float done = fminf(w.TE[j] + w.TR[j], 1.f);
+            float a = fmaf(p.gamma * w.TR[j], w.B[j], w.R[j]);
+            if (p.next_values) a = fmaf(g1l * (1.f - done), w.NV[j], a);
             float bb = gl * (1.f - done);
-            if (s.edge[j]) {
-                float carry = 0.f;
-                if (s.valid[j] && p.bootstrap_values)
-                    carry = p.truncateds ? B[j] : p.bootstrap_values[s.flat[j]];
-                a = fmaf(bb, carry, a);
+            if (bit(gr.edges, j)) {
+                a = fmaf(bb, w.B[j] + w.EB[j], a);  // carry G_T = B_{T-1}
                 bb = 0.f;
             }
-            al[j] = s.valid[j] ? a : 0.f;
-            be[j] = s.valid[j] ? bb : 1.f;
+            al[j] = bit(gr.valid, j) ? a : 0.f;
+            be[j] = bit(gr.valid, j) ? bb : 1.f;
         }
     }
 
-    __device__ void epilogue(const Geo& g, const Slots<G>& s, const float (&A)[G],
-                             const float (&)[G], const float (&)[G], const Keep (&)[G]) const {
-        store_group<G, true>(p.out, g, s, A);
+    template <bool FAST>
+    __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
+                             const float (&)[G], const Keep (&)[G]) const {
+        store_group<G, true, FAST>(p.out + tl.lo, gr, A);
     }
 };
 
@@ -205,39 +265,53 @@ struct PrefixOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = false;
     PrefixArgs p;
+    struct Raw {
+        float X[G], D[G], S[G];
+        float halo;
+    };
     struct Keep {};
+    __device__ size_t lds_floats_per_wave() const { return 0; }
 
-    __device__ void prologue(const Geo& g, const SegInfo& si, const Slots<G>& s, float (&al)[G],
-                             float (&be)[G], Keep (&)[G]) const {
-        float X[G], D[G];
-        load_group<G, false>(p.inputs, g, s, X);
-        load_group<G, false>(p.dones, g, s, D);
-        float DP[G];
-        if (!p.starts_at) {
-            const float halo = (lane_id() == 0 && si.halo_valid) ? p.dones[si.halo_flat] : 0.f;
-            scan_prev<G>(D, halo, DP);
+    template <bool FAST>
+    __device__ void load(const Geo& g, const Tile& tl, const SegInfo& si, const Grp& gr,
+                         Raw& w) const {
+        load_group<G, false, FAST>(p.inputs + tl.lo, gr, w.X);
+        load_group<G, false, FAST>(p.dones + tl.lo, gr, w.D);
+#pragma unroll
+        for (int j = 0; j < G; ++j) w.S[j] = 0.f;
+        if (p.seed && (gr.edges & gr.valid)) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                if (bit(gr.edges & gr.valid, j)) w.S[j] = p.seed[row_at(g, tl, gr.off + j)];
         }
+        w.halo = (!p.starts_at && lane_id() == 0 && si.halo_valid) ? p.dones[si.halo_flat] : 0.f;
+    }
+
+    __device__ void coeffs(const Grp& gr, const Raw& w, float (&al)[G], float (&be)[G],
+                           Keep (&)[G]) const {
+        float DP[G];
+        scan_prev<G>(w.D, w.halo, DP);
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            float gate = p.starts_at ? 1.f - D[j] : 1.f - DP[j];
-            float a = X[j];
+            float gate = p.starts_at ? 1.f - w.D[j] : 1.f - DP[j];
+            float a = w.X[j];
             float bb;
-            if (s.edge[j]) {
+            if (bit(gr.edges, j)) {
                 if (!p.starts_at) gate = 1.f;  // d_{-1} = 0
-                const float seed = (p.seed && s.valid[j]) ? p.seed[s.row[j]] : 0.f;
-                a = fmaf(p.decay * gate, seed, a);
+                a = fmaf(p.decay * gate, w.S[j], a);
                 bb = 0.f;
             } else {
                 bb = p.decay * gate;
             }
-            al[j] = s.valid[j] ? a : 0.f;
-            be[j] = s.valid[j] ? bb : 1.f;
+            al[j] = bit(gr.valid, j) ? a : 0.f;
+            be[j] = bit(gr.valid, j) ? bb : 1.f;
         }
     }
 
-    __device__ void epilogue(const Geo& g, const Slots<G>& s, const float (&A)[G],
-                             const float (&)[G], const float (&)[G], const Keep (&)[G]) const {
-        store_group<G, false>(p.out, g, s, A);
+    template <bool FAST>
+    __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
+                             const float (&)[G], const Keep (&)[G]) const {
+        store_group<G, false, FAST>(p.out + tl.lo, gr, A);
     }
 };
 
@@ -256,20 +330,43 @@ struct RetraceOp {
     static constexpr int G = 1;
     static constexpr bool BACKWARD = true;
     RetraceArgs p;
+    struct Raw {
+        float mu, q, r, te, tr;
+        int64_t act;
+        float c_h, q_h;  // halo: c and q of the scan-previous element (lane 0)
+    };
     struct Keep {
         float q, u, k;
     };
+    __device__ size_t lds_floats_per_wave() const { return 2 * (size_t)kWave * (size_t)p.A; }
 
-    __device__ float trace_weight_at(int64_t f, float* ratio_out) const {
-        int64_t a = p.actions[f];
-        a = a < 0 ? 0 : (a >= p.A ? p.A - 1 : a);
-        const float ratio = p.pi_target[f * p.A + a] / p.mu_taken[f];
-        if (ratio_out) *ratio_out = ratio;
-        return p.lambda * fminf(p.c_bar, ratio);
+    __device__ int64_t clamp_action(int64_t a) const { return a < 0 ? 0 : (a >= p.A ? p.A - 1 : a); }
+
+    template <bool FAST>
+    __device__ void load(const Geo&, const Tile& tl, const SegInfo& si, const Grp& gr,
+                         Raw& w) const {
+        const bool valid = bit(gr.valid, 0);
+        const int64_t f = tl.lo + gr.off;
+        w.mu = valid ? p.mu_taken[f] : 1.f;
+        w.q = valid ? p.q_taken[f] : 0.f;
+        w.r = valid ? p.rewards[f] : 0.f;
+        w.te = valid ? p.terminateds[f] : 0.f;
+        w.tr = (valid && p.truncateds) ? p.truncateds[f] : 0.f;
+        w.act = valid ? clamp_action(p.actions[f]) : 0;
+        w.c_h = 0.f;
+        w.q_h = 0.f;
+        if (lane_id() == 0 && si.halo_valid) {
+            const int64_t h = si.halo_flat;
+            const int64_t a = clamp_action(p.actions[h]);
+            w.c_h = p.lambda * fminf(p.c_bar, p.pi_target[h * p.A + a] / p.mu_taken[h]);
+            w.q_h = p.q_taken[h];
+        }
     }
 
-    __device__ void prologue(const Geo& g, const SegInfo& si, const Slots<G>& s, float (&al)[G],
-                             float (&be)[G], Keep (&kp)[G]) const {
+    // Stages the segment's pi and pi*Q slab in LDS and returns E_t and pi[t,a_t]
+    // for this lane's step.  Called by every lane of the workgroup.
+    __device__ void expectation(const Geo& g, const Tile& tl, const SegInfo& si, const Grp& gr,
+                                const Raw& w, float& expect, float& pia) const {
         const int lane = lane_id();
         const int A = (int)p.A;
         float* lpi = si.lds;
@@ -303,120 +400,120 @@ struct RetraceOp {
             }
         }
         __syncthreads();
-
-        const bool valid = s.valid[0];
-        const int64_t f = s.flat[0];
-        const int tau = (int)(f - si.seg_lo);
-        float expect = 0.f, pia = 0.f, mu = 1.f, q = 0.f, r = 0.f, te = 0.f, tr = 0.f;
-        if (valid) {
+        expect = 0.f;
+        pia = 0.f;
+        if (bit(gr.valid, 0)) {
+            const int tau = (int)(tl.lo + gr.off - si.seg_lo);
             const float* row = lprod + tau * A;
             for (int a = 0; a < A; ++a) expect += row[a];
-            int64_t act = p.actions[f];
-            act = act < 0 ? 0 : (act >= p.A ? p.A - 1 : act);
-            pia = lpi[tau * A + (int)act];
-            mu = p.mu_taken[f];
-            q = p.q_taken[f];
-            r = p.rewards[f];
-            te = p.terminateds[f];
-            if (p.truncateds) tr = p.truncateds[f];
+            pia = lpi[tau * A + (int)w.act];
         }
-        const float ratio = pia / mu;
-        const float c = p.lambda * fminf(p.c_bar, ratio);
-        const float rho = fminf(p.rho_bar, ratio);
-
-        float c_h = 0.f, q_h = 0.f;
-        if (lane == 0 && si.halo_valid) {
-            c_h = trace_weight_at(si.halo_flat, nullptr);
-            q_h = p.q_taken[si.halo_flat];
-        }
-        const float c_next = wave_shift_prev(c, c_h);
-        const float q_next = wave_shift_prev(q, q_h);
-
-        const float done = fminf(te + tr, 1.f);
-        const bool edge = s.edge[0];
-        const float a = fmaf(p.gamma * (1.f - te), expect, r) - q;
-        const float bb = edge ? 0.f : p.gamma * c_next * (1.f - done);  // c_T = 0
-        al[0] = valid ? a : 0.f;
-        be[0] = valid ? bb : 1.f;
-        kp[0].q = q;
-        kp[0].u = edge ? rho * (r - q) : rho * fmaf(p.gamma * (1.f - te), q_next, r - q);
-        kp[0].k = edge ? 0.f : rho * p.gamma * (1.f - te);
     }
 
-    __device__ void epilogue(const Geo& g, const Slots<G>& s, const float (&A)[G],
-                             const float (&prevA)[G], const float (&)[G], const Keep (&kp)[G]) const {
-        if (!s.valid[0]) return;
-        const int64_t f = s.flat[0];
+    __device__ void finish(const Grp& gr, const Raw& w, float expect, float pia, float (&al)[G],
+                           float (&be)[G], Keep (&kp)[G]) const {
+        const float ratio = pia / w.mu;
+        const float c = p.lambda * fminf(p.c_bar, ratio);
+        const float rho = fminf(p.rho_bar, ratio);
+        const float c_next = wave_shift_prev(c, w.c_h);
+        const float q_next = wave_shift_prev(w.q, w.q_h);
+        const float done = fminf(w.te + w.tr, 1.f);
+        const bool edge = bit(gr.edges, 0);
+        const float a = fmaf(p.gamma * (1.f - w.te), expect, w.r) - w.q;
+        const float bb = edge ? 0.f : p.gamma * c_next * (1.f - done);  // c_T = 0
+        al[0] = bit(gr.valid, 0) ? a : 0.f;
+        be[0] = bit(gr.valid, 0) ? bb : 1.f;
+        kp[0].q = w.q;
+        kp[0].u = edge ? rho * (w.r - w.q) : rho * fmaf(p.gamma * (1.f - w.te), q_next, w.r - w.q);
+        kp[0].k = edge ? 0.f : rho * p.gamma * (1.f - w.te);
+    }
+
+    template <bool FAST>
+    __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G],
+                             const float (&prevA)[G], const float (&)[G],
+                             const Keep (&kp)[G]) const {
+        if (!bit(gr.valid, 0)) return;
+        const int64_t f = tl.lo + gr.off;
         p.q_ret[f] = A[0] + kp[0].q;
         if (p.advantages) p.advantages[f] = fmaf(kp[0].k, prevA[0], kp[0].u);
     }
 };
 
+template <class Op>
+struct IsRetrace {
+    static constexpr bool value = false;
+};
+template <>
+struct IsRetrace<RetraceOp> {
+    static constexpr bool value = true;
+};
+
 // ---------------------------------------------------------------------------
 // The shared kernel
 // ---------------------------------------------------------------------------
-template <class Op, int WAVES, int SEGS, bool LOOKBACK>
-__global__ __launch_bounds__(WAVES * kWave) void scan_kernel(Op op, Geo g, uint8_t* ws) {
+struct TileShared {
+    float wave_a[8], wave_b[8];
+    float carry;
+};
+
+template <class Op, int WAVES, int SEGS, bool LOOKBACK, bool FAST>
+__device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile& tl, uint8_t* ws,
+                                          int64_t q, uint32_t epoch, TileShared& sh,
+                                          float* lds_wave) {
     constexpr int G = Op::G;
     constexpr bool BACKWARD = Op::BACKWARD;
     constexpr int SEG = kWave * G;
     constexpr int TILE = WAVES * SEGS * SEG;
     using Keep = typename Op::Keep;
-
-    __shared__ float s_wave_a[WAVES], s_wave_b[WAVES];
-    __shared__ float s_carry;
-    __shared__ uint32_t s_tile, s_epoch;
-    extern __shared__ __align__(16) float s_dyn[];
+    using Raw = typename Op::Raw;
 
     const int lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
 
-    int64_t q;  // tile index in scan order
-    uint32_t epoch = 0;
-    if constexpr (LOOKBACK) {
-        if (threadIdx.x == 0) {
-            uint32_t t, e;
-            claim_tile(reinterpret_cast<uint32_t*>(ws), t, e);
-            s_tile = t;
-            s_epoch = e;
-        }
-        __syncthreads();
-        q = s_tile;
-        epoch = s_epoch;
-    } else {
-        q = blockIdx.x;
-    }
-    const int64_t k = BACKWARD ? (g.num_tiles - 1 - q) : q;
-    const int64_t tile_lo = k * (int64_t)TILE;
-    const int64_t row_lo = tile_lo / g.T;
-    const int64_t t_lo = tile_lo - row_lo * g.T;
-
-    float al[SEGS][G], be[SEGS][G];
-    Keep kp[SEGS][G];
-    Affine incl[SEGS], segtot[SEGS];
-    float* lds_wave = s_dyn + (size_t)wave * op.lds_floats_per_wave();
-
+    // segment s of this wave covers tile offsets [seg_off(s), seg_off(s) + SEG)
+    auto seg_off = [&](int s) -> uint32_t {
+        const int idx = wave * SEGS + s;  // segment index in scan order
+        return BACKWARD ? (uint32_t)(TILE - (idx + 1) * SEG) : (uint32_t)(idx * SEG);
+    };
     auto seg_info = [&](int s) {
-        const int64_t idx = (int64_t)wave * SEGS + s;  // segment index in scan order
         SegInfo si;
-        si.seg_lo = BACKWARD ? tile_lo + TILE - (idx + 1) * SEG : tile_lo + idx * SEG;
+        si.seg_lo = tl.lo + seg_off(s);
         si.halo_flat = BACKWARD ? si.seg_lo + SEG : si.seg_lo - 1;
         si.halo_valid = si.halo_flat >= 0 && si.halo_flat < g.N;
         si.lds = lds_wave;
         return si;
     };
-    auto lane_slots = [&](const SegInfo& si, Slots<G>& sl) {
-        const int64_t gflat = BACKWARD ? si.seg_lo + SEG - G - (int64_t)lane * G
-                                       : si.seg_lo + (int64_t)lane * G;
-        make_slots<G, BACKWARD>(g, tile_lo, row_lo, t_lo, TILE, gflat, sl);
+    auto lane_grp = [&](int s) {
+        const uint32_t off = seg_off(s) + (BACKWARD ? (uint32_t)(SEG - G - lane * G)
+                                                    : (uint32_t)(lane * G));
+        return make_grp<G, BACKWARD, FAST>(g, tl, off);
     };
 
+    // phase 1: issue every load of every segment
+    Raw raw[SEGS];
+    uint32_t edges[SEGS];
 #pragma unroll
     for (int s = 0; s < SEGS; ++s) {
-        const SegInfo si = seg_info(s);
-        Slots<G> sl;
-        lane_slots(si, sl);
-        op.prologue(g, si, sl, al[s], be[s], kp[s]);
+        const Grp gr = lane_grp(s);
+        edges[s] = gr.edges;
+        op.template load<FAST>(g, tl, seg_info(s), gr, raw[s]);
+    }
+
+    // phase 2: coefficients and the scan inside the wave
+    float al[SEGS][G], be[SEGS][G];
+    Keep kp[SEGS][G];
+    Affine incl[SEGS], segtot[SEGS];
+#pragma unroll
+    for (int s = 0; s < SEGS; ++s) {
+        Grp gr = lane_grp(s);
+        gr.edges = edges[s];
+        if constexpr (IsRetrace<Op>::value) {
+            float expect, pia;
+            op.expectation(g, tl, seg_info(s), gr, raw[s], expect, pia);
+            op.finish(gr, raw[s], expect, pia, al[s], be[s], kp[s]);
+        } else {
+            op.coeffs(gr, raw[s], al[s], be[s], kp[s]);
+        }
         Affine agg{al[s][0], be[s][0]};
 #pragma unroll
         for (int j = 1; j < G; ++j) agg = compose(Affine{al[s][j], be[s][j]}, agg);
@@ -428,42 +525,42 @@ __global__ __launch_bounds__(WAVES * kWave) void scan_kernel(Op op, Geo g, uint8
 #pragma unroll
     for (int s = 1; s < SEGS; ++s) wtot = compose(segtot[s], wtot);
 
+    // across the waves of the workgroup
     Affine wexcl = identity_map();
     Affine ttot = wtot;
     if constexpr (WAVES > 1) {
         if (lane == 0) {
-            s_wave_a[wave] = wtot.a;
-            s_wave_b[wave] = wtot.b;
+            sh.wave_a[wave] = wtot.a;
+            sh.wave_b[wave] = wtot.b;
         }
         __syncthreads();
         Affine acc = identity_map();
 #pragma unroll
         for (int u = 0; u < WAVES; ++u) {
             if (u == wave) wexcl = acc;
-            acc = compose(Affine{s_wave_a[u], s_wave_b[u]}, acc);
+            acc = compose(Affine{sh.wave_a[u], sh.wave_b[u]}, acc);
         }
         ttot = acc;
     }
 
+    // across workgroups
     float x = 0.f;
     if constexpr (LOOKBACK) {
-        const int64_t tile_hi = tile_lo + TILE;
-        const bool need_carry = BACKWARD ? (tile_hi < g.N && tile_hi % g.T != 0)
-                                         : (tile_lo % g.T != 0);
+        const int64_t tile_hi = tl.lo + TILE;
+        const bool need_carry = BACKWARD ? (tile_hi < g.N && tile_hi % g.T != 0) : (tl.t_lo != 0);
         if (wave == 0) x = lookback(ws, epoch, q, ttot, need_carry);
         if constexpr (WAVES > 1) {
-            if (threadIdx.x == 0) s_carry = x;
+            if (threadIdx.x == 0) sh.carry = x;
             __syncthreads();
-            x = s_carry;
+            x = sh.carry;
         }
     }
 
+    // phase 3: apply the carries and write the outputs
     float xs = fmaf(wexcl.b, x, wexcl.a);  // value entering this wave's first segment
 #pragma unroll
     for (int s = 0; s < SEGS; ++s) {
-        const SegInfo si = seg_info(s);
-        Slots<G> sl;
-        lane_slots(si, sl);
+        const Grp gr = lane_grp(s);
         const float ea = wave_shift_prev(incl[s].a, 0.f);
         const float eb = wave_shift_prev(incl[s].b, 1.f);
         float y = fmaf(eb, xs, ea);  // value entering this lane's first element
@@ -474,12 +571,38 @@ __global__ __launch_bounds__(WAVES * kWave) void scan_kernel(Op op, Geo g, uint8
             A[j] = fmaf(be[s][j], y, al[s][j]);
             y = A[j];
         }
-        op.epilogue(g, sl, A, prevA, al[s], kp[s]);
+        op.template epilogue<FAST>(tl, gr, A, prevA, al[s], kp[s]);
         xs = fmaf(segtot[s].b, xs, segtot[s].a);
     }
+}
+
+template <class Op, int WAVES, int SEGS, bool LOOKBACK>
+__global__ __launch_bounds__(WAVES * kWave) void scan_kernel(Op op, Geo g, uint8_t* ws) {
+    constexpr int TILE = WAVES * SEGS * kWave * Op::G;
+    static_assert(WAVES <= 8, "TileShared holds eight waves");
+    __shared__ TileShared sh;
+    extern __shared__ __align__(16) float s_dyn[];
+
+    const int64_t q = blockIdx.x;  // tile index in scan order
+    uint32_t epoch = 0;
+    if constexpr (LOOKBACK) epoch = read_epoch(ws);
+    float* lds_wave = s_dyn + (size_t)(threadIdx.x / kWave) * op.lds_floats_per_wave();
+    Tile tl;
+    tl.lo = (Op::BACKWARD ? (g.num_tiles - 1 - q) : q) * (int64_t)TILE;
+    tl.row_lo = tl.lo / g.T;
+    tl.t_lo = (uint32_t)(tl.lo - tl.row_lo * g.T);
+    const int64_t rem = g.N - tl.lo;
+    tl.rem = rem >= TILE ? (uint32_t)TILE : (uint32_t)rem;
+    tl.elems = TILE;
+    const bool fast = g.vec_ok && rem >= TILE;
+    if (fast)
+        scan_tile<Op, WAVES, SEGS, LOOKBACK, true>(op, g, tl, ws, q, epoch, sh, lds_wave);
+    else
+        scan_tile<Op, WAVES, SEGS, LOOKBACK, false>(op, g, tl, ws, q, epoch, sh, lds_wave);
 
     if constexpr (LOOKBACK) {
-        if (threadIdx.x == 0) retire_tile(reinterpret_cast<uint32_t*>(ws), (uint32_t)g.num_tiles, epoch);
+        __syncthreads();
+        if (threadIdx.x == 0) retire_tile(ws, q, g.num_tiles, epoch);
     }
 }
 
@@ -518,72 +641,56 @@ rlscan_status launch_cfg(const Op& op, const Geo& g, bool lookback, void* ws, si
 
 template <class Op>
 rlscan_status launch_g4(const Op& op, const Plan& plan, void* ws, hipStream_t stream) {
-    switch (plan.tile) {
-        case 256: return launch_cfg<Op, 1, 1>(op, plan.geo, plan.lookback, ws, 0, stream);
-        case 1024: return launch_cfg<Op, 1, 4>(op, plan.geo, plan.lookback, ws, 0, stream);
-        case 4096: return launch_cfg<Op, 4, 4>(op, plan.geo, plan.lookback, ws, 0, stream);
-        default: return set_error(RLSCAN_ERR_BAD_PARAM, "internal: unsupported tile size");
-    }
+    const int w = plan.waves, t = plan.tile;
+    if (t == 256 && w == 1) return launch_cfg<Op, 1, 1>(op, plan.geo, plan.lookback, ws, 0, stream);
+    if (t == 1024 && w == 1) return launch_cfg<Op, 1, 4>(op, plan.geo, plan.lookback, ws, 0, stream);
+    if (t == 2048 && w == 4) return launch_cfg<Op, 4, 2>(op, plan.geo, plan.lookback, ws, 0, stream);
+    if (t == 4096 && w == 4) return launch_cfg<Op, 4, 4>(op, plan.geo, plan.lookback, ws, 0, stream);
+    if (t == 4096 && w == 8) return launch_cfg<Op, 8, 2>(op, plan.geo, plan.lookback, ws, 0, stream);
+    return set_error(RLSCAN_ERR_BAD_PARAM, "internal: unsupported tile configuration");
 }
 
 }  // namespace
 
-// Dynamic LDS per wave (floats): only Retrace stages a slab in LDS.
-struct GaeK : GaeOp {
-    __device__ size_t lds_floats_per_wave() const { return 0; }
-};
-struct VtraceK : VtraceOp {
-    __device__ size_t lds_floats_per_wave() const { return 0; }
-};
-struct ReturnsK : ReturnsOp {
-    __device__ size_t lds_floats_per_wave() const { return 0; }
-};
-struct PrefixK : PrefixOp {
-    __device__ size_t lds_floats_per_wave() const { return 0; }
-};
-struct RetraceK : RetraceOp {
-    __device__ size_t lds_floats_per_wave() const { return 2 * (size_t)kWave * (size_t)p.A; }
-};
-
 rlscan_status launch_gae(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s) {
-    GaeK op;
+    GaeOp op;
     op.p = a;
     return launch_g4(op, plan, ws, s);
 }
 
 rlscan_status launch_vtrace(const VtraceArgs& a, const Plan& plan, void* ws, hipStream_t s) {
-    VtraceK op;
+    VtraceOp op;
     op.p = a;
     return launch_g4(op, plan, ws, s);
 }
 
 rlscan_status launch_returns(const ReturnsArgs& a, const Plan& plan, void* ws, hipStream_t s) {
-    ReturnsK op;
+    ReturnsOp op;
     op.p = a;
     return launch_g4(op, plan, ws, s);
 }
 
 rlscan_status launch_prefix(const PrefixArgs& a, const Plan& plan, void* ws, hipStream_t s) {
-    PrefixK op;
+    PrefixOp op;
     op.p = a;
     return launch_g4(op, plan, ws, s);
 }
 
 rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s) {
-    RetraceK op;
+    RetraceOp op;
     op.p = a;
     const size_t lds = (size_t)plan.waves * 2 * kWave * (size_t)a.A * sizeof(float);
     if (plan.waves == 4 && plan.tile == 1024)
-        return launch_cfg<RetraceK, 4, 4>(op, plan.geo, plan.lookback, ws, lds, s);
+        return launch_cfg<RetraceOp, 4, 4>(op, plan.geo, plan.lookback, ws, lds, s);
     if (plan.waves == 1 && plan.tile == 1024)
-        return launch_cfg<RetraceK, 1, 16>(op, plan.geo, plan.lookback, ws, lds, s);
+        return launch_cfg<RetraceOp, 1, 16>(op, plan.geo, plan.lookback, ws, lds, s);
     if (plan.waves == 1 && plan.tile == 256)
-        return launch_cfg<RetraceK, 1, 4>(op, plan.geo, plan.lookback, ws, lds, s);
+        return launch_cfg<RetraceOp, 1, 4>(op, plan.geo, plan.lookback, ws, lds, s);
     return set_error(RLSCAN_ERR_BAD_PARAM, "internal: unsupported retrace tile");
 }
 
 rlscan_status launch_debug_wave_scan(const float* a, const float* b, float* oa, float* ob,
-                                    int num_waves, hipStream_t s) {
+                                     int num_waves, hipStream_t s) {
     hipLaunchKernelGGL(debug_wave_scan_kernel, dim3((unsigned)num_waves), dim3(kWave), 0, s, a, b,
                        oa, ob);
     const hipError_t err = hipGetLastError();

@@ -22,7 +22,9 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "librlscan.so")
+# RLSCAN_LIBRARY may point at another build of the same library (for example
+# one compiled with different cache hints); there is no fallback.
+LIB_PATH = os.environ.get("RLSCAN_LIBRARY") or os.path.join(_HERE, "librlscan.so")
 
 RLSCAN_OK = 0
 RLSCAN_ENDS_AT = 0
