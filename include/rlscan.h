@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define RLSCAN_ABI_VERSION 1
+#define RLSCAN_ABI_VERSION 2
 
 typedef struct ihipStream_t* rlscan_stream_t; /* same type as hipStream_t */
 
@@ -61,7 +61,8 @@ typedef enum rlscan_status {
     RLSCAN_ERR_BAD_PARAM = 3, /* a scalar or enum argument is invalid */
     RLSCAN_ERR_CONFLICT = 4,  /* mutually exclusive optional arguments were both given */
     RLSCAN_ERR_WORKSPACE = 5, /* the call needs a workspace and none or too small a one was given */
-    RLSCAN_ERR_LAUNCH = 6     /* the HIP runtime refused the kernel launch */
+    RLSCAN_ERR_LAUNCH = 6,    /* the HIP runtime refused the kernel launch */
+    RLSCAN_ERR_DATA = 7       /* rlscan_check_inputs found inputs that break the contract */
 } rlscan_status;
 
 typedef enum rlscan_boundary {
@@ -92,6 +93,49 @@ rlscan_status rlscan_workspace_init(void* ws, size_t ws_bytes, rlscan_stream_t s
  * Non-zero means a look-back wait exceeded its bound and the affected
  * outputs are invalid; the word is sticky until rlscan_workspace_init. */
 rlscan_status rlscan_workspace_error(const void* ws, uint32_t* error_out, rlscan_stream_t stream);
+
+/*
+ * Debug data checks, off the hot path.  The rl-triton pages keep two costly
+ * input checks behind a correctness-warnings switch (kernels page, argument
+ * checks of compute_gae and compute_vtrace; GAE page, "The unifying rule"):
+ * no step may be both terminated and truncated, and when truncateds is given,
+ * bootstrap_values must be zero at every interior step that is not
+ * truncated (a stray value there would be added to the successor value).
+ * This call runs those checks, plus the two that the kernels' contract
+ * relies on: flags are exactly 0.0f or 1.0f, and actions lie in
+ * [0, num_actions).  Over the arrays given (each may be NULL) it counts
+ *   flags_not_binary      entries of terminateds or truncateds that are
+ *                         neither 0.0f nor 1.0f (NaN included);
+ *   term_and_trunc        steps where terminateds != 0 and truncateds != 0;
+ *   stray_bootstrap       with truncateds and bootstrap_values both given:
+ *                         steps t < T-1 where truncateds == 0 and
+ *                         bootstrap_values != 0;
+ *   actions_out_of_range  entries of actions (int64) outside [0, num_actions).
+ * Pass a forward scan's dones as `terminateds`.
+ * The call is SYNCHRONOUS (it waits for `stream`) and must not be captured
+ * in a graph.  It keeps its counters in 32 bytes of the header of a
+ * workspace (256-byte aligned, at least rlscan_workspace_bytes(1, 1) bytes)
+ * and clears them itself; the look-back state in that workspace is left as
+ * it was, so the workspace of the estimator calls can be passed.
+ * Returns RLSCAN_OK when every count is zero and RLSCAN_ERR_DATA otherwise
+ * (rlscan_last_error() names the failed checks).  `report` (host memory, or
+ * NULL) receives the counts in both cases.
+ * Errors  all four arrays NULL -> NULL_ARG; E, T out of range, or actions
+ *         given with num_actions < 1 -> BAD_SHAPE; ws NULL, misaligned or too
+ *         small -> WORKSPACE; a failed launch or copy -> LAUNCH.
+ */
+typedef struct rlscan_check_report {
+    int64_t flags_not_binary;
+    int64_t term_and_trunc;
+    int64_t stray_bootstrap;
+    int64_t actions_out_of_range;
+} rlscan_check_report;
+
+rlscan_status rlscan_check_inputs(const float* terminateds, const float* truncateds,
+                                  const float* bootstrap_values, const int64_t* actions,
+                                  int64_t num_envs, int64_t seq_len, int64_t num_actions,
+                                  void* ws, size_t ws_bytes, rlscan_check_report* report,
+                                  rlscan_stream_t stream);
 
 /*
  * GAE -- rl-triton kernels page, API Reference: compute_gae (Recurrence);

@@ -1,8 +1,9 @@
 """Builds librlscan.so in-tree with hipcc for gfx950.
 
 Usage: ``python -m linear_recurrence_scan_amd.build`` (or ``build()`` from
-Python).  The shared object lands next to this file, where the ctypes binding
-looks for it.
+Python).  Each HIP source compiles to its own object, in parallel; the host
+API is compiled and everything linked into one shared object next to this
+file, where the ctypes binding looks for it.
 """
 from __future__ import annotations
 
@@ -10,11 +11,15 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librlscan.so")
-SOURCES = ["rlscan_kernels.hip", "rlscan_api.cpp"]
+HIP_SOURCES = ["op_gae.hip", "op_vtrace.hip", "op_returns.hip", "op_prefix.hip",
+               "op_retrace.hip", "aux_kernels.hip"]
+HOST_SOURCES = ["rlscan_api.cpp"]
 ARCH = os.environ.get("RLSCAN_OFFLOAD_ARCH", "gfx950")
 
 
@@ -25,31 +30,42 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: install ROCm or set HIPCC")
 
 
-def command(out: str, defines=()) -> list[str]:
+def _common(defines) -> list[str]:
     return [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         "-Wall", "-Wno-unused-parameter",
         # packed fp32 VALU forms stay disabled in every HIP translation unit
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         *[f"-D{d}" for d in defines],
-        "-x", "hip", *[os.path.join(CSRC, s) for s in SOURCES],
-        "-o", out,
     ]
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    tmp = out + f".tmp{os.getpid()}"
-    cmd = command(tmp, defines)
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
     if proc.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stderr[-6000:]}")
-    if verbose and proc.stderr.strip():
-        print(proc.stderr[-3000:], file=sys.stderr)
-    os.replace(tmp, out)
+        raise RuntimeError(f"hipcc failed ({proc.returncode}): {' '.join(cmd[-3:])}\n"
+                           f"{proc.stderr[-6000:]}")
+    return proc
+
+
+def build(verbose: bool = False, out: str = LIB, defines=(), csrc: str = CSRC) -> str:
+    """Compiles every source under `csrc` and links `out`.  Returns `out`."""
+    with tempfile.TemporaryDirectory(prefix="rlscan_build_") as tmp:
+        jobs = []
+        for src in HIP_SOURCES + HOST_SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            jobs.append((_common(defines) + ["-c", "-x", "hip", os.path.join(csrc, src), "-o", obj],
+                         obj))
+        workers = min(len(jobs), max(1, min(os.cpu_count() or 1, 8)))
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            list(pool.map(lambda j: _run(j[0], verbose), jobs))
+        tmp_out = out + f".tmp{os.getpid()}"
+        _run(_common(defines) + ["-shared", *[o for _, o in jobs], "-o", tmp_out], verbose)
+        os.replace(tmp_out, out)
     return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,84 @@
+// aux_kernels.hip -- small kernels around the estimator scans: workspace
+// fill, the debug data checks, and the bare wave-scan primitive exported for
+// layout tests.
+#include "rlscan_internal.hpp"
+#include "scan_core.hpp"
+
+namespace rlscan {
+
+__global__ void debug_wave_scan_kernel(const float* a, const float* b, float* oa, float* ob) {
+    const size_t i = (size_t)blockIdx.x * kWave + threadIdx.x;
+    const Affine r = wave_inclusive_scan(Affine{a[i], b[i]});
+    oa[i] = r.a;
+    ob[i] = r.b;
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// Data-contract checks (debug path, not tuned): one grid-stride pass over the
+// flat [E,T] range, per-thread counts reduced in LDS, one global atomic per
+// workgroup and counter, and only when that count is nonzero.
+__global__ void check_kernel(const float* term, const float* trunc, const float* boot,
+                             const int64_t* actions, int64_t N, int64_t T, int64_t A,
+                             unsigned long long* counts) {
+    unsigned long long c[4] = {0, 0, 0, 0};
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < N;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const float te = term ? term[i] : 0.f;
+        const float tr = trunc ? trunc[i] : 0.f;
+        if (term && !(te == 0.f || te == 1.f)) c[0]++;
+        if (trunc && !(tr == 0.f || tr == 1.f)) c[0]++;
+        if (term && trunc && te != 0.f && tr != 0.f) c[1]++;
+        if (trunc && boot && tr == 0.f && (i % T) != T - 1 && boot[i] != 0.f) c[2]++;
+        if (actions) {
+            const int64_t a = actions[i];
+            if (a < 0 || a >= A) c[3]++;
+        }
+    }
+    __shared__ unsigned long long s_counts[4];
+    if (threadIdx.x < 4) s_counts[threadIdx.x] = 0;
+    __syncthreads();
+    for (int k = 0; k < 4; ++k)
+        if (c[k]) atomicAdd(&s_counts[k], c[k]);
+    __syncthreads();
+    if (threadIdx.x < 4 && s_counts[threadIdx.x]) atomicAdd(&counts[threadIdx.x], s_counts[threadIdx.x]);
+}
+
+rlscan_status launch_debug_wave_scan(const float* a, const float* b, float* oa, float* ob,
+                                     int num_waves, hipStream_t s) {
+    hipLaunchKernelGGL(debug_wave_scan_kernel, dim3((unsigned)num_waves), dim3(kWave), 0, s, a, b,
+                       oa, ob);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
+    return RLSCAN_OK;
+}
+
+rlscan_status launch_check(const float* term, const float* trunc, const float* boot,
+                           const int64_t* actions, int64_t N, int64_t T, int64_t A,
+                           unsigned long long* counts, hipStream_t s) {
+    int64_t blocks = (N + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(check_kernel, dim3((unsigned)blocks), dim3(256), 0, s, term, trunc, boot,
+                       actions, N, T, A, counts);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
+    return RLSCAN_OK;
+}
+
+rlscan_status launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+    const size_t words = bytes / 4;
+    if (words == 0) return RLSCAN_OK;
+    size_t blocks = (words + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       static_cast<uint32_t*>(p), words);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
+    return RLSCAN_OK;
+}
+
+}  // namespace rlscan

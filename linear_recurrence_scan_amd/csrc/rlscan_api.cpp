@@ -17,7 +17,7 @@ thread_local char g_last_error[512] = "";
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Launch-shape override for tuning experiments: RLSCAN_CFG="tile,waves" with
-// one of 256,1 / 1024,1 / 2048,4 / 4096,4 / 4096,8.
+// one of 256,1 / 2048,4 / 4096,4 / 4096,8.
 bool cfg_override(int& tile, int& waves) {
     static int cached_tile = -1, cached_waves = 0;
     if (cached_tile < 0) {
@@ -25,7 +25,7 @@ bool cfg_override(int& tile, int& waves) {
         const char* s = std::getenv("RLSCAN_CFG");
         int t = 0, w = 0;
         if (s && std::sscanf(s, "%d,%d", &t, &w) == 2) {
-            const bool ok = (t == 256 && w == 1) || (t == 1024 && w == 1) || (t == 2048 && w == 4) ||
+            const bool ok = (t == 256 && w == 1) || (t == 2048 && w == 4) ||
                             (t == 4096 && w == 4) || (t == 4096 && w == 8);
             if (ok) {
                 cached_tile = t;
@@ -44,6 +44,27 @@ constexpr int kMinTile = 256;
 
 size_t ws_bytes_for_tiles(int64_t tiles) {
     return (size_t)WsHeader::kSlotsByteOffset + (size_t)tiles * 32u;
+}
+
+// Fills in the geometry of a launch of `tile`-element tiles.  A look-back is
+// needed when a row spans tiles or tiles straddle rows.  When every row is a
+// whole number (>= 2) of tiles and there are several rows, the tiles run
+// column-major (tile j of every row before tile j + 1 of any), which puts
+// E launches between a tile and its scan predecessor.
+rlscan_status finish_plan(int64_t E, int64_t T, int tile, int waves, bool vec_ok, Plan& plan) {
+    const int64_t N = E * T;
+    plan.tile = tile;
+    plan.waves = waves;
+    plan.geo.N = N;
+    plan.geo.rows = E;
+    plan.geo.T = (uint32_t)T;
+    plan.geo.num_tiles = (N + tile - 1) / tile;
+    plan.geo.magic = T < tile ? (uint32_t)(0xFFFFFFFFu / (uint32_t)T) : 0u;
+    plan.geo.vec_ok = vec_ok ? 1 : 0;
+    plan.lookback = plan.geo.num_tiles > 1 && (tile % T) != 0;
+    plan.geo.interleave = (plan.lookback && E > 1 && T % tile == 0) ? 1 : 0;
+    if (plan.geo.num_tiles >= kMaxTiles) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
+    return RLSCAN_OK;
 }
 
 // Plans a launch of a 4-elements-per-lane kernel.
@@ -67,16 +88,7 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
             waves = 4;
         }
     }
-    plan.tile = tile;
-    plan.waves = waves;
-    plan.geo.N = N;
-    plan.geo.T = (uint32_t)T;
-    plan.geo.num_tiles = (N + tile - 1) / tile;
-    plan.geo.magic = T < tile ? (uint32_t)(0xFFFFFFFFu / (uint32_t)T) : 0u;
-    plan.geo.vec_ok = vec_ok ? 1 : 0;
-    plan.lookback = plan.geo.num_tiles > 1 && (tile % T) != 0;
-    if (plan.geo.num_tiles >= kMaxTiles) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
-    return RLSCAN_OK;
+    return finish_plan(E, T, tile, waves, vec_ok, plan);
 }
 
 rlscan_status plan_retrace(int64_t E, int64_t T, int64_t A, Plan& plan, bool vec_ok) {
@@ -87,16 +99,7 @@ rlscan_status plan_retrace(int64_t E, int64_t T, int64_t A, Plan& plan, bool vec
         tile = 256;
         waves = 1;
     }
-    plan.tile = tile;
-    plan.waves = waves;
-    plan.geo.N = N;
-    plan.geo.T = (uint32_t)T;
-    plan.geo.num_tiles = (N + tile - 1) / tile;
-    plan.geo.magic = T < tile ? (uint32_t)(0xFFFFFFFFu / (uint32_t)T) : 0u;
-    plan.geo.vec_ok = vec_ok ? 1 : 0;
-    plan.lookback = plan.geo.num_tiles > 1 && (tile % T) != 0;
-    if (plan.geo.num_tiles >= kMaxTiles) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
-    return RLSCAN_OK;
+    return finish_plan(E, T, tile, waves, vec_ok, plan);
 }
 
 rlscan_status check_shape(int64_t E, int64_t T) {
@@ -152,6 +155,7 @@ const char* rlscan_status_string(rlscan_status status) {
         case RLSCAN_ERR_CONFLICT: return "conflicting optional arguments";
         case RLSCAN_ERR_WORKSPACE: return "missing or too small workspace";
         case RLSCAN_ERR_LAUNCH: return "kernel launch failed";
+        case RLSCAN_ERR_DATA: return "inputs break the data contract";
     }
     return "unknown status";
 }
@@ -182,6 +186,48 @@ rlscan_status rlscan_workspace_error(const void* ws, uint32_t* error_out, rlscan
         err = hipMemcpy(error_out, static_cast<const uint8_t*>(ws) + 4 * WsHeader::kError,
                         sizeof(uint32_t), hipMemcpyDeviceToHost);
     if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
+    return RLSCAN_OK;
+}
+
+rlscan_status rlscan_check_inputs(const float* terminateds, const float* truncateds,
+                                  const float* bootstrap_values, const int64_t* actions,
+                                  int64_t num_envs, int64_t seq_len, int64_t num_actions,
+                                  void* ws, size_t ws_bytes, rlscan_check_report* report,
+                                  rlscan_stream_t stream) {
+    if (!terminateds && !truncateds && !bootstrap_values && !actions)
+        return set_error(RLSCAN_ERR_NULL_ARG, "give at least one array to check");
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (actions && num_actions < 1)
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_actions must be >= 1 when actions are given");
+    if (!ws) return set_error(RLSCAN_ERR_WORKSPACE, "rlscan_check_inputs needs a workspace");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return set_error(RLSCAN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < (size_t)WsHeader::kSlotsByteOffset)
+        return set_error(RLSCAN_ERR_WORKSPACE, "workspace smaller than its header");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint8_t* counters = static_cast<uint8_t*>(ws) + 4 * WsHeader::kCheck;
+    RLSCAN_TRY(launch_fill_zero(counters, 4 * sizeof(unsigned long long), s));
+    RLSCAN_TRY(launch_check(terminateds, truncateds, bootstrap_values, actions,
+                            num_envs * seq_len, seq_len, num_actions,
+                            reinterpret_cast<unsigned long long*>(counters), s));
+    unsigned long long host[4] = {0, 0, 0, 0};
+    hipError_t err = hipMemcpyAsync(host, counters, sizeof(host), hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
+    if (report) {
+        report->flags_not_binary = (int64_t)host[0];
+        report->term_and_trunc = (int64_t)host[1];
+        report->stray_bootstrap = (int64_t)host[2];
+        report->actions_out_of_range = (int64_t)host[3];
+    }
+    if (host[0] | host[1] | host[2] | host[3]) {
+        char msg[256];
+        std::snprintf(msg, sizeof(msg),
+                      "flags not 0/1: %llu; terminated and truncated: %llu; stray bootstrap "
+                      "values: %llu; actions out of range: %llu",
+                      host[0], host[1], host[2], host[3]);
+        return set_error(RLSCAN_ERR_DATA, msg);
+    }
     return RLSCAN_OK;
 }
 

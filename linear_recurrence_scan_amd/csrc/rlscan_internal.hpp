@@ -63,6 +63,11 @@ rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, h
 rlscan_status launch_returns(const ReturnsArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_prefix(const PrefixArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Counts contract violations into four u64 counters (zeroed by the caller's
+// stream order beforehand); see rlscan_check_inputs.
+rlscan_status launch_check(const float* term, const float* trunc, const float* boot,
+                           const int64_t* actions, int64_t N, int64_t T, int64_t A,
+                           unsigned long long* counts, hipStream_t s);
 rlscan_status launch_debug_wave_scan(const float* a, const float* b, float* oa, float* ob,
                                     int num_waves, hipStream_t s);
 

@@ -59,6 +59,12 @@ __device__ __forceinline__ float readlane(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+__device__ __forceinline__ uint64_t readfirstlane_u64(uint64_t x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // One Hillis-Steele step.  A lane whose source lane does not exist (shifted
 // in from outside its 16-lane row, or a row the row mask leaves out) keeps
 // DPP's "old" operand, which is the identity map, so the combine is a no-op
@@ -103,9 +109,11 @@ __device__ __forceinline__ void scan_prev(const float (&x)[G], float halo, float
 struct Geo {
     int64_t N;          // E*T elements
     int64_t num_tiles;  // ceil(N / TILE)
+    int64_t rows;       // E
     uint32_t T;         // row length (< 2^31)
     uint32_t magic;     // floor((2^32-1)/T) when T < tile, for the small-T division
     int vec_ok;         // every [E,T] pointer is 16-byte aligned
+    int interleave;     // rows are whole multiples of the tile and tiles run column-major
 };
 
 // Quotient of x / T for x < 2^31 using a precomputed reciprocal; exact after
@@ -258,10 +266,9 @@ __device__ __forceinline__ void store_group(float* __restrict__ tp, const Grp& g
 // Decoupled look-back across the workgroups of one launch
 // ---------------------------------------------------------------------------
 // Workspace layout (bytes):
-//   [0]    epoch u32 (advanced once per call by the last workgroup to finish)
-//   [64]   finish counter of the top level u32
-//   [128]  error word u32
-//   [256]  64 leaf finish counters, one per 64-byte line
+//   [128]  error word u32 (sticky; set when a look-back wait exceeds its bound)
+//   [192]  4 x u64 counters of rlscan_check_inputs
+//   [256]  64 epoch leaves, one u64 per 64-byte line: (epoch << 32) | tickets
 //   [4352] 32 bytes per tile in scan order: aggregate a, aggregate b,
 //          inclusive value, unused.
 // Every slot is a 64-bit word (tag << 32 | float bits) written and read with
@@ -269,20 +276,26 @@ __device__ __forceinline__ void store_group(float* __restrict__ tp, const Grp& g
 // also sees the value; tags 2*epoch+1 (aggregate) and 2*epoch+2 (inclusive)
 // never match a zero-filled slot or one left by an earlier call.
 //
-// Tile q of a launch is workgroup q (scan order).  A tile waits only for
-// tiles with smaller q, and every tile publishes its aggregate (and, when its
-// map does not depend on the carry, its inclusive value) before it waits for
-// anything, so the wait ends as soon as the lower-numbered workgroups have
-// run their local scans.  Finishing is counted in a two-level tree (tile q
-// counts into leaf q % 64, the last of each leaf counts into the top) so no
-// address takes more than 64 atomic increments per call: one address
-// serialises device-scope atomics at roughly 11 ns each on this chip.
+// A tile waits only for tiles with smaller scan index, and every tile
+// publishes its aggregate (and, when its map does not depend on the carry,
+// its inclusive value) before it waits for anything, so the wait ends as soon
+// as its predecessors have run their local scans.
+//
+// The epoch.  Tile q takes a ticket from leaf q % 64 with one atomic add,
+// issued when the tile starts and not waited for until its look-back, so its
+// latency hides behind the tile's data loads.  The add returns the leaf's
+// epoch and the ticket number together; the tile holding a leaf's last ticket
+// of the call moves that leaf to the next epoch with its count reset, and
+// tile 0 does the same for the leaves no tile of the call uses.  All 64
+// leaves therefore move together, once per call, and a workgroup never waits
+// on an atomic before it exits.  Spreading the tickets over 64 addresses
+// matters: one address serialises device-scope atomics at roughly 11 ns each
+// on this chip.
 struct WsHeader {
-    static constexpr int kEpoch = 0;     // u32 index
-    static constexpr int kTop = 16;      // u32 index (64 bytes)
-    static constexpr int kError = 32;    // u32 index (128 bytes)
-    static constexpr int kLeaf0 = 64;    // u32 index of leaf 0 (256 bytes)
-    static constexpr int kLeafStride = 16;  // u32 per leaf (64 bytes)
+    static constexpr int kError = 32;            // u32 index (128 bytes)
+    static constexpr int kCheck = 48;            // u32 index (192 bytes): 4 x u64 counters
+    static constexpr int kLeafByte0 = 256;       // byte offset of leaf 0
+    static constexpr int kLeafStrideBytes = 64;  // one leaf per 64-byte line
     static constexpr int kLeaves = 64;
     static constexpr int kSlotsByteOffset = 256 + 64 * 64;
 };
@@ -301,45 +314,95 @@ __device__ __forceinline__ uint64_t slot_load(const uint64_t* p) {
 __device__ __forceinline__ uint32_t tag_of(uint64_t w) { return (uint32_t)(w >> 32); }
 __device__ __forceinline__ float val_of(uint64_t w) { return __uint_as_float((uint32_t)w); }
 
-__device__ __forceinline__ uint32_t read_epoch(uint8_t* ws) {
-    return __hip_atomic_load(reinterpret_cast<uint32_t*>(ws) + WsHeader::kEpoch, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t* leaf_word(uint8_t* ws, int leaf) {
+    return reinterpret_cast<uint64_t*>(ws + WsHeader::kLeafByte0 + leaf * WsHeader::kLeafStrideBytes);
 }
 
-// Called by one thread of tile q after the workgroup is done with the
-// workspace.  The last tile to finish resets the counters and advances the
-// epoch for the next call.
-__device__ __forceinline__ void retire_tile(uint8_t* ws, int64_t q, int64_t num_tiles, uint32_t epoch) {
-    uint32_t* hdr = reinterpret_cast<uint32_t*>(ws);
+// Takes tile q's ticket (one lane).  Returns the leaf word before the add.
+__device__ __forceinline__ uint64_t epoch_ticket(uint8_t* ws, int64_t q) {
+    return __hip_atomic_fetch_add(leaf_word(ws, (int)(q % WsHeader::kLeaves)), 1ull,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Moves the leaves on to the next epoch (one lane, once its ticket has
+// returned): the holder of a leaf's last ticket of the call resets that leaf,
+// tile 0 the leaves no tile of the call draws from.
+__device__ __forceinline__ void epoch_advance(uint8_t* ws, int64_t q, int64_t num_tiles,
+                                              uint64_t ticket) {
     const int leaf = (int)(q % WsHeader::kLeaves);
-    const uint32_t leaf_total = (uint32_t)((num_tiles - leaf + WsHeader::kLeaves - 1) / WsHeader::kLeaves);
-    uint32_t* lc = hdr + WsHeader::kLeaf0 + leaf * WsHeader::kLeafStride;
-    const uint32_t n = __hip_atomic_fetch_add(lc, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (n != leaf_total - 1) return;
-    const uint32_t top_total = (uint32_t)(num_tiles < WsHeader::kLeaves ? num_tiles : WsHeader::kLeaves);
-    const uint32_t m = __hip_atomic_fetch_add(hdr + WsHeader::kTop, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-    if (m != top_total - 1) return;
-    for (uint32_t l = 0; l < top_total; ++l)
-        __hip_atomic_store(hdr + WsHeader::kLeaf0 + l * WsHeader::kLeafStride, 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(hdr + WsHeader::kTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(hdr + WsHeader::kEpoch, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t leaf_total =
+        (uint64_t)((num_tiles - leaf + WsHeader::kLeaves - 1) / WsHeader::kLeaves);
+    const uint64_t next = (uint64_t)((uint32_t)(ticket >> 32) + 1u) << 32;
+    if ((ticket & 0xffffffffull) == leaf_total - 1)
+        __hip_atomic_store(leaf_word(ws, leaf), next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (q == 0)
+        for (int64_t l = num_tiles; l < WsHeader::kLeaves; ++l)
+            __hip_atomic_store(leaf_word(ws, (int)l), next, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One lane's view of the look-back window: the slot of the tile (1 + lane)
+// steps back in scan order (scan index q - (1 + lane) * stride), all three
+// words read with independent loads (one memory round trip).
+struct LookbackView {
+    uint64_t a = 0, b = 0, inc = 0;
+};
+
+__device__ __forceinline__ LookbackView lookback_read(uint8_t* ws, int64_t q, int64_t stride) {
+    const uint64_t* slots = reinterpret_cast<const uint64_t*>(ws + WsHeader::kSlotsByteOffset);
+    const int64_t j = q - (1 + lane_id()) * stride;
+    LookbackView v;
+    if (j >= 0) {
+        v.inc = slot_load(slots + 4 * j + 2);
+        v.a = slot_load(slots + 4 * j + 0);
+        v.b = slot_load(slots + 4 * j + 1);
+    }
+    return v;
+}
+
+// The scan predecessor's inclusive word (every lane; one broadcast load).
+__device__ __forceinline__ uint64_t lookback_read_prev(uint8_t* ws, int64_t q, int64_t stride) {
+    const uint64_t* slots = reinterpret_cast<const uint64_t*>(ws + WsHeader::kSlotsByteOffset);
+    return q >= stride ? slot_load(slots + 4 * (q - stride) + 2) : 0ull;
+}
+
+// Tries to evaluate the carry from one view of the window: it needs a
+// published inclusive value at some lane `first` and an aggregate (or
+// inclusive) at every lane before it.  The carry is then nested outward-in,
+// x <- a_j + b_j * x, from that inclusive value.  Called by all 64 lanes.
+__device__ __forceinline__ bool lookback_resolve(const LookbackView& v, uint32_t epoch, float& x) {
+    const uint32_t tag_agg = 2u * epoch + 1u;
+    const uint32_t tag_inc = 2u * epoch + 2u;
+    const bool inc = tag_of(v.inc) == tag_inc;
+    const bool agg = tag_of(v.a) == tag_agg && tag_of(v.b) == tag_agg;
+    const uint64_t inc_mask = __ballot(inc);
+    if (inc_mask == 0) return false;
+    const uint64_t ok_mask = __ballot(inc || agg);
+    const int first = __ffsll((unsigned long long)inc_mask) - 1;
+    const uint64_t need = first == 63 ? ~0ull : ((1ull << (first + 1)) - 1ull);
+    if ((ok_mask & need) != need) return false;
+    const float va = agg ? val_of(v.a) : 0.f;
+    const float vb = agg ? val_of(v.b) : 1.f;
+    x = readlane(val_of(v.inc), first);
+    for (int i = first - 1; i >= 0; --i) x = fmaf(readlane(vb, i), x, readlane(va, i));
+    return true;
 }
 
 // Publishes tile q's total map and returns the value entering the tile (the
-// inclusive value of tile q-1 in scan order).  Called by all 64 lanes of one
+// inclusive value of its scan predecessor, tile q - stride).  Called by all 64 lanes of one
 // wave.  need_carry == false means the tile's first scan element starts a row
 // segment (its beta is 0), so nothing enters and no waiting is needed.
+// `early` is tile q-1's inclusive word as read before the tile's own scan:
+// when it is already published the carry is known without another memory
+// round trip; otherwise the window of predecessors is polled.
 //
-// The carry is evaluated by nesting x <- a_j + b_j * x outward-in from the
-// nearest predecessor whose inclusive value is published, over at most 63
-// aggregates read in one wave-wide pass.  Every inclusive value is therefore
-// the same fixed function of the inputs whatever the timing, and results are
+// Every inclusive value is the same fixed function of the inputs whatever the
+// timing (the nesting always starts from the nearest published inclusive
+// value, and a tile publishes its inclusive value only once), so results are
 // bitwise reproducible.  Waits are bounded: past kSpinLimit polls the error
 // word is set and the tile proceeds with a zero carry.
-__device__ __forceinline__ float lookback(uint8_t* ws, uint32_t epoch, int64_t q, Affine tot,
-                                          bool need_carry) {
+__device__ __forceinline__ float lookback(uint8_t* ws, uint32_t epoch, int64_t q, int64_t stride,
+                                          Affine tot, bool need_carry, uint64_t early) {
     uint64_t* slots = reinterpret_cast<uint64_t*>(ws + WsHeader::kSlotsByteOffset);
     uint32_t* hdr = reinterpret_cast<uint32_t*>(ws);
     const uint32_t tag_agg = 2u * epoch + 1u;
@@ -356,46 +419,20 @@ __device__ __forceinline__ float lookback(uint8_t* ws, uint32_t epoch, int64_t q
         slot_store(mine + 1, tag_agg, tot.b);
     }
 
-    float x = 0.f;
-    uint32_t spins = 0;
-    for (;;) {
-        const int64_t j = q - 1 - lane;
-        bool inc = false, agg = false;
-        float va = 0.f, vb = 1.f, vi = 0.f;
-        if (j >= 0) {
-            const uint64_t wi = slot_load(slots + 4 * j + 2);
-            if (tag_of(wi) == tag_inc) {
-                inc = true;
-                vi = val_of(wi);
-            } else {
-                const uint64_t wa = slot_load(slots + 4 * j + 0);
-                const uint64_t wb = slot_load(slots + 4 * j + 1);
-                if (tag_of(wa) == tag_agg && tag_of(wb) == tag_agg) {
-                    agg = true;
-                    va = val_of(wa);
-                    vb = val_of(wb);
-                }
-            }
-        }
-        const uint64_t inc_mask = __ballot(inc);
-        const uint64_t ok_mask = __ballot(inc || agg);
-        if (inc_mask != 0) {
-            const int first = __ffsll((unsigned long long)inc_mask) - 1;
-            const uint64_t need = first == 63 ? ~0ull : ((1ull << (first + 1)) - 1ull);
-            if ((ok_mask & need) == need) {
-                x = readlane(vi, first);
-                for (int i = first - 1; i >= 0; --i) x = fmaf(readlane(vb, i), x, readlane(va, i));
+    float x = val_of(early);
+    if (tag_of(early) != tag_inc) {
+        uint32_t spins = 0;
+        for (;;) {
+            if (lookback_resolve(lookback_read(ws, q, stride), epoch, x)) break;
+            if (++spins > kSpinLimit) {
+                if (lane == 0)
+                    __hip_atomic_fetch_or(hdr + WsHeader::kError, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                x = 0.f;
                 break;
             }
+            __builtin_amdgcn_s_sleep(1);
         }
-        if (++spins > kSpinLimit) {
-            if (lane == 0)
-                __hip_atomic_fetch_or(hdr + WsHeader::kError, 1u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
-            x = 0.f;
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
     }
     if (tot.b != 0.f && lane == 0) slot_store(mine + 2, tag_inc, fmaf(tot.b, x, tot.a));
     return x;

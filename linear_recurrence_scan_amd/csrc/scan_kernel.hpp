@@ -1,0 +1,283 @@
+// scan_kernel.hpp -- the one templated kernel every estimator runs, and its
+// launcher.  Each estimator (op_*.hip) supplies an Op with
+//   G, BACKWARD                 elements per lane and scan direction
+//   Raw, Keep                   raw inputs of one lane's G elements, and what
+//                               the epilogue needs besides the scan result
+//   lds_floats_per_wave()       dynamic LDS per wave (0 unless staged)
+//   load<FAST>(...)             issue this lane's loads for one segment
+//   coeffs(...) or              build (alpha, beta) in registers
+//     expectation()+finish()    (Retrace: slab staged through LDS first)
+//   epilogue<FAST>(...)         write the outputs from the scanned values
+// and the kernel runs, per tile:
+//   1. load:     every input of every segment the wave owns is requested
+//                before any arithmetic, so a wave keeps all its reads in
+//                flight at once;
+//   2. coeffs:   alpha/beta in registers, lane fold, DPP wave scan, LDS
+//                across waves, look-back across workgroups;
+//   3. epilogue: carries applied, outputs written.
+// Nothing is materialised in HBM between those steps (rl-triton paper,
+// Sec. 4.2, Table 2).
+//
+// Row boundaries are handled by folding the row's boundary carry into alpha
+// and setting beta = 0 at the row's first scan element (paper, Sec. 3.2 and
+// Table 1 "Bootstrap" column), which lets one tile hold several short rows or
+// one long row span several tiles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "rlscan_internal.hpp"
+#include "scan_core.hpp"
+
+namespace rlscan {
+
+// Inputs a call may omit.  Each Op is compiled once per combination it
+// supports, so an absent stream costs neither a load nor a register.
+enum : unsigned {
+    kTrunc = 1u,         // truncateds given
+    kBoot2D = 2u,        // full [E,T] bootstrap_values read alongside (with truncateds)
+    kNextValues = 4u,    // TD(lambda) next_values given
+    kLogpBehavior = 8u,  // V-trace log_pi_behavior given
+};
+
+struct SegInfo {
+    int64_t seg_lo;     // lowest flat index of the segment
+    int64_t halo_flat;  // scan-previous element of the segment's first scan element
+    bool halo_valid;
+    float* lds;         // this wave's dynamic LDS (staged ops only)
+};
+
+// Continuation value at a row end when it does not come from a full [E,T]
+// bootstrap array read alongside the other inputs: last_value[row], or
+// column T-1 of bootstrap_values when there are no truncations.
+__device__ __forceinline__ float edge_bootstrap(const float* last_value, const float* boot,
+                                                int64_t row, int64_t flat) {
+    return last_value ? last_value[row] : boot[flat];
+}
+
+template <class Op>
+struct IsStaged {
+    static constexpr bool value = false;
+};
+
+struct TileShared {
+    float wave_a[8], wave_b[8];
+    float carry;
+};
+
+template <class Op, int WAVES, int SEGS, bool LOOKBACK, bool FAST>
+__device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile& tl, uint8_t* ws,
+                                          int64_t q, int64_t stride, uint64_t ticket,
+                                          TileShared& sh, float* lds_wave) {
+    constexpr int G = Op::G;
+    constexpr bool BACKWARD = Op::BACKWARD;
+    constexpr int SEG = kWave * G;
+    constexpr int TILE = WAVES * SEGS * SEG;
+    using Keep = typename Op::Keep;
+    using Raw = typename Op::Raw;
+
+    const int lane = lane_id();
+    const int wave = (int)(threadIdx.x / kWave);
+
+    // segment s of this wave covers tile offsets [seg_off(s), seg_off(s) + SEG)
+    auto seg_off = [&](int s) -> uint32_t {
+        const int idx = wave * SEGS + s;  // segment index in scan order
+        return BACKWARD ? (uint32_t)(TILE - (idx + 1) * SEG) : (uint32_t)(idx * SEG);
+    };
+    auto seg_info = [&](int s) {
+        SegInfo si;
+        si.seg_lo = tl.lo + seg_off(s);
+        si.halo_flat = BACKWARD ? si.seg_lo + SEG : si.seg_lo - 1;
+        si.halo_valid = si.halo_flat >= 0 && si.halo_flat < g.N;
+        si.lds = lds_wave;
+        return si;
+    };
+    auto lane_grp = [&](int s) {
+        const uint32_t off = seg_off(s) + (BACKWARD ? (uint32_t)(SEG - G - lane * G)
+                                                    : (uint32_t)(lane * G));
+        return make_grp<G, BACKWARD, FAST>(g, tl, off);
+    };
+
+    // phase 1: issue every load of every segment
+    Raw raw[SEGS];
+    uint32_t edges[SEGS];
+#pragma unroll
+    for (int s = 0; s < SEGS; ++s) {
+        const Grp gr = lane_grp(s);
+        edges[s] = gr.edges;
+        op.template load<FAST>(g, tl, seg_info(s), gr, raw[s]);
+    }
+
+    // A tile whose first scan element starts a row segment needs no carry.
+    bool need_carry = false;
+    uint64_t early = 0;
+    if constexpr (LOOKBACK) {
+        const int64_t tile_hi = tl.lo + TILE;
+        need_carry = BACKWARD ? (tile_hi < g.N && tile_hi % g.T != 0) : (tl.t_lo != 0);
+        // First look at the predecessor's inclusive value, issued behind the
+        // data loads: once the predecessor has finished, the carry is known
+        // without another memory round trip.
+        if (wave == 0 && need_carry) early = lookback_read_prev(ws, q, stride);
+    }
+
+    // phase 2: coefficients and the scan inside the wave
+    float al[SEGS][G], be[SEGS][G];
+    Keep kp[SEGS][G];
+    Affine incl[SEGS], segtot[SEGS];
+#pragma unroll
+    for (int s = 0; s < SEGS; ++s) {
+        Grp gr = lane_grp(s);
+        gr.edges = edges[s];
+        if constexpr (IsStaged<Op>::value) {
+            float expect, pia;
+            op.expectation(g, tl, seg_info(s), gr, raw[s], expect, pia);
+            op.finish(gr, raw[s], expect, pia, al[s], be[s], kp[s]);
+        } else {
+            op.coeffs(gr, raw[s], al[s], be[s], kp[s]);
+        }
+        Affine agg{al[s][0], be[s][0]};
+#pragma unroll
+        for (int j = 1; j < G; ++j) agg = compose(Affine{al[s][j], be[s][j]}, agg);
+        incl[s] = wave_inclusive_scan(agg);
+        segtot[s] = Affine{readlane(incl[s].a, kWave - 1), readlane(incl[s].b, kWave - 1)};
+    }
+
+    Affine wtot = segtot[0];
+#pragma unroll
+    for (int s = 1; s < SEGS; ++s) wtot = compose(segtot[s], wtot);
+
+    // across the waves of the workgroup
+    Affine wexcl = identity_map();
+    Affine ttot = wtot;
+    if constexpr (WAVES > 1) {
+        if (lane == 0) {
+            sh.wave_a[wave] = wtot.a;
+            sh.wave_b[wave] = wtot.b;
+        }
+        __syncthreads();
+        Affine acc = identity_map();
+#pragma unroll
+        for (int u = 0; u < WAVES; ++u) {
+            if (u == wave) wexcl = acc;
+            acc = compose(Affine{sh.wave_a[u], sh.wave_b[u]}, acc);
+        }
+        ttot = acc;
+    }
+
+    // across workgroups
+    float x = 0.f;
+    if constexpr (LOOKBACK) {
+        if (wave == 0) {
+            const uint64_t t = readfirstlane_u64(ticket);
+            if (lane == 0) epoch_advance(ws, q, g.num_tiles, t);
+            x = lookback(ws, (uint32_t)(t >> 32), q, stride, ttot, need_carry, early);
+        }
+        if constexpr (WAVES > 1) {
+            if (threadIdx.x == 0) sh.carry = x;
+            __syncthreads();
+            x = sh.carry;
+        }
+    }
+
+    // phase 3: apply the carries and write the outputs
+    float xs = fmaf(wexcl.b, x, wexcl.a);  // value entering this wave's first segment
+#pragma unroll
+    for (int s = 0; s < SEGS; ++s) {
+        const Grp gr = lane_grp(s);
+        const float ea = wave_shift_prev(incl[s].a, 0.f);
+        const float eb = wave_shift_prev(incl[s].b, 1.f);
+        float y = fmaf(eb, xs, ea);  // value entering this lane's first element
+        float A[G], prevA[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            prevA[j] = y;
+            A[j] = fmaf(be[s][j], y, al[s][j]);
+            y = A[j];
+        }
+        op.template epilogue<FAST>(tl, gr, A, prevA, al[s], kp[s]);
+        xs = fmaf(segtot[s].b, xs, segtot[s].a);
+    }
+}
+
+// Occupancy the register allocator is held to.  An op whose eight elements
+// per lane fit 64 VGPRs without spilling (Op::kFits64) is held to 8 waves per
+// SIMD in its look-back-free kernels; every other kernel takes what the
+// allocator gives (1 = no constraint).
+template <class Op, int SEGS, bool LOOKBACK>
+struct WavesPerEu {
+    static constexpr int value = (Op::kFits64 && !LOOKBACK && SEGS * Op::G <= 8) ? 8 : 1;
+};
+
+template <class Op, int WAVES, int SEGS, bool LOOKBACK>
+__global__ __launch_bounds__(WAVES * kWave)
+__attribute__((amdgpu_waves_per_eu(WavesPerEu<Op, SEGS, LOOKBACK>::value))) void scan_kernel(
+    Op op, Geo g, uint8_t* ws) {
+    constexpr int TILE = WAVES * SEGS * kWave * Op::G;
+    static_assert(WAVES <= 8, "TileShared holds eight waves");
+    __shared__ TileShared sh;
+    extern __shared__ __align__(16) float s_dyn[];
+
+    const int64_t q = blockIdx.x;  // tile index in scan order
+    // Every tile of a look-back launch takes its epoch ticket first; the add
+    // completes while the tile's data loads are in flight.
+    uint64_t ticket = 0;
+    if constexpr (LOOKBACK)
+        if (threadIdx.x == 0) ticket = epoch_ticket(ws, q);
+    float* lds_wave = s_dyn + (size_t)(threadIdx.x / kWave) * op.lds_floats_per_wave();
+
+    // Scan order to flat tiles.  Row-major: tile q is the q-th tile of the
+    // flat array in scan direction, its predecessor is q - 1.  Column-major
+    // (rows of whole tiles): tile q is tile j = q / E of row r = q % E, so
+    // the tiles that start rows run first and a tile's predecessor, q - E,
+    // was launched E workgroups earlier and is usually done by the time the
+    // tile needs its carry.
+    int64_t ftile, stride = 1;
+    if (g.interleave) {
+        const int64_t r = q % g.rows, j = q / g.rows;
+        const int64_t per_row = (int64_t)g.T / TILE;
+        ftile = r * per_row + (Op::BACKWARD ? per_row - 1 - j : j);
+        stride = g.rows;
+    } else {
+        ftile = Op::BACKWARD ? g.num_tiles - 1 - q : q;
+    }
+    Tile tl;
+    tl.lo = ftile * (int64_t)TILE;
+    tl.row_lo = tl.lo / g.T;
+    tl.t_lo = (uint32_t)(tl.lo - tl.row_lo * g.T);
+    const int64_t rem = g.N - tl.lo;
+    tl.rem = rem >= TILE ? (uint32_t)TILE : (uint32_t)rem;
+    tl.elems = TILE;
+    const bool fast = g.vec_ok && rem >= TILE;
+    if (fast)
+        scan_tile<Op, WAVES, SEGS, LOOKBACK, true>(op, g, tl, ws, q, stride, ticket, sh, lds_wave);
+    else
+        scan_tile<Op, WAVES, SEGS, LOOKBACK, false>(op, g, tl, ws, q, stride, ticket, sh, lds_wave);
+}
+
+template <class Op, int WAVES, int SEGS>
+rlscan_status launch_cfg(const Op& op, const Geo& g, bool lookback, void* ws, size_t lds_bytes,
+                         hipStream_t stream) {
+    const dim3 grid((unsigned)g.num_tiles), block(WAVES * kWave);
+    if (lookback)
+        hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, true>), grid, block, lds_bytes, stream, op,
+                           g, static_cast<uint8_t*>(ws));
+    else
+        hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, false>), grid, block, lds_bytes, stream, op,
+                           g, static_cast<uint8_t*>(ws));
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
+    return RLSCAN_OK;
+}
+
+// Launch shapes of the four-elements-per-lane ops (tile = WAVES*SEGS*256).
+template <class Op>
+rlscan_status launch_g4(const Op& op, const Plan& plan, void* ws, hipStream_t stream) {
+    const int w = plan.waves, t = plan.tile;
+    if (t == 256 && w == 1) return launch_cfg<Op, 1, 1>(op, plan.geo, plan.lookback, ws, 0, stream);
+    if (t == 2048 && w == 4) return launch_cfg<Op, 4, 2>(op, plan.geo, plan.lookback, ws, 0, stream);
+    if (t == 4096 && w == 4) return launch_cfg<Op, 4, 4>(op, plan.geo, plan.lookback, ws, 0, stream);
+    if (t == 4096 && w == 8) return launch_cfg<Op, 8, 2>(op, plan.geo, plan.lookback, ws, 0, stream);
+    return set_error(RLSCAN_ERR_BAD_PARAM, "internal: unsupported tile configuration");
+}
+
+}  // namespace rlscan

@@ -12,6 +12,8 @@ Two layers, same names as the C ABI plus the reference-style helpers:
   * gae / vtrace / retrace / lambda_returns / discounted_returns /
     eligibility_traces / episodic_prefix_sum: allocate outputs and follow the
     rl-triton keyword conventions (kernels page, API Reference).
+check_inputs runs the debug data checks (rlscan_check_inputs); with
+RLSCAN_CHECKS=1 in the environment every helper runs them before its call.
 """
 from __future__ import annotations
 
@@ -27,12 +29,19 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("RLSCAN_LIBRARY") or os.path.join(_HERE, "librlscan.so")
 
 RLSCAN_OK = 0
+RLSCAN_ERR_DATA = 7
 RLSCAN_ENDS_AT = 0
 RLSCAN_STARTS_AT = 1
 
 _lib = None
 _lock = threading.Lock()
 _workspaces: dict = {}
+
+
+class CheckReport(ctypes.Structure):
+    """Mirror of rlscan_check_report."""
+    _fields_ = [("flags_not_binary", ctypes.c_int64), ("term_and_trunc", ctypes.c_int64),
+                ("stray_bootstrap", ctypes.c_int64), ("actions_out_of_range", ctypes.c_int64)]
 
 
 class RLScanError(RuntimeError):
@@ -71,8 +80,11 @@ def _declare(L):
     L.rlscan_returns.argtypes = [vp] * 6 + [i64, i64, f32, f32, vp, sz, vp]
     L.rlscan_prefix.argtypes = [vp] * 4 + [i64, i64, f32, ctypes.c_int, vp, sz, vp]
     L.rlscan_debug_wave_scan.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
-    for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error", "rlscan_gae", "rlscan_vtrace",
-                 "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
+    L.rlscan_check_inputs.argtypes = [vp] * 4 + [i64, i64, i64, vp, sz,
+                                                 ctypes.POINTER(CheckReport), vp]
+    for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
+                 "rlscan_gae", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
+                 "rlscan_check_inputs"):
         getattr(L, name).restype = st
     return L
 
@@ -142,6 +154,52 @@ def workspace_error(device=None):
     _check("rlscan_workspace_error", lib().rlscan_workspace_error(_ptr(ws), ctypes.byref(out),
                                                                   _stream(device)))
     return int(out.value)
+
+
+def check_inputs(terminateds=None, truncateds=None, bootstrap_values=None, actions=None,
+                 num_actions=0):
+    """Runs rlscan_check_inputs (synchronous) and returns its counts as a dict
+    with an extra key "ok".  Arrays must share one [num_envs, seq_len] shape."""
+    given = [t for t in (terminateds, truncateds, bootstrap_values, actions) if t is not None]
+    if not given:
+        raise ValueError("give at least one array to check")
+    E, T = _shape2("arrays", given[0])
+    dev = given[0].device
+    te = _f32("terminateds", terminateds, (E, T), dev, optional=True)
+    tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
+    bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
+    act = None
+    if actions is not None:
+        if not isinstance(actions, torch.Tensor) or actions.dtype != torch.int64:
+            raise TypeError("actions must be an int64 tensor")
+        if tuple(actions.shape) != (E, T) or actions.device != dev:
+            raise ValueError("actions must be [num_envs, seq_len] on the same device")
+        act = actions.contiguous()
+    ws, nws = workspace(dev, E, T)
+    rep = CheckReport()
+    st = lib().rlscan_check_inputs(_ptr(te), _ptr(tr), _ptr(bv), _ptr(act), E, T, int(num_actions),
+                                   _ptr(ws), nws, ctypes.byref(rep), _stream(dev))
+    if st not in (RLSCAN_OK, RLSCAN_ERR_DATA):
+        _check("rlscan_check_inputs", st)
+    out = {name: int(getattr(rep, name)) for name, _ in CheckReport._fields_}
+    out["ok"] = st == RLSCAN_OK
+    return out
+
+
+def _checks_enabled():
+    return os.environ.get("RLSCAN_CHECKS", "0") not in ("", "0")
+
+
+def _debug_check(func, **arrays):
+    """With RLSCAN_CHECKS=1 in the environment, validates the data before a
+    call and raises ValueError on a contract violation (off by default: the
+    check synchronises the stream)."""
+    if not _checks_enabled():
+        return
+    rep = check_inputs(**arrays)
+    if not rep["ok"]:
+        bad = ", ".join(f"{k}={v}" for k, v in rep.items() if k != "ok" and v)
+        raise ValueError(f"{func}: inputs break the data contract ({bad})")
 
 
 # ---------------------------------------------------------------------------
@@ -227,6 +285,7 @@ def gae(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
     tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
     bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
     lv = _f32("last_value", last_value, (E,), dev, optional=True)
+    _debug_check("gae", terminateds=te, truncateds=tr, bootstrap_values=bv)
     adv = torch.empty_like(r)
     ret = torch.empty_like(r) if want_returns else None
     rlscan_gae(r, v, te, tr, bv, lv, adv, ret, gamma, lambda_)
@@ -247,6 +306,7 @@ def vtrace(log_pi_target, log_pi_behavior, values, rewards, terminateds, truncat
     tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
     bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
     lv = _f32("last_value", last_value, (E,), dev, optional=True)
+    _debug_check("vtrace", terminateds=te, truncateds=tr, bootstrap_values=bv)
     vs = torch.empty_like(r)
     pg = torch.empty_like(r)
     rlscan_vtrace(lpt, lpb, v, r, te, tr, bv, lv, vs, pg, gamma, rho_bar, c_bar)
@@ -273,6 +333,7 @@ def retrace(action_probs_target, action_probs_behavior, q_values, next_q_values_
     if tuple(actions.shape) != (E, T) or actions.device != dev:
         raise ValueError("actions must be [num_envs, seq_len] on the same device")
     act = actions.contiguous()
+    _debug_check("retrace", terminateds=te, truncateds=tr, actions=act, num_actions=A)
     q_ret = torch.empty_like(r)
     adv = torch.empty_like(r)
     rlscan_retrace(pi, mu, q, qn, act, r, te, tr, q_ret, adv, gamma, lambda_, c_bar, rho_bar)
@@ -289,6 +350,7 @@ def lambda_returns(rewards, next_values, terminateds, truncateds=None, gamma=0.9
     te = _f32("terminateds", terminateds, (E, T), dev)
     tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
     bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
+    _debug_check("lambda_returns", terminateds=te, truncateds=tr, bootstrap_values=bv)
     out = torch.empty_like(r)
     rlscan_returns(r, nv, te, tr, bv, out, gamma, lambda_)
     return out
@@ -302,6 +364,7 @@ def discounted_returns(rewards, terminateds, truncateds=None, gamma=0.99, bootst
     te = _f32("terminateds", terminateds, (E, T), dev)
     tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
     bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
+    _debug_check("discounted_returns", terminateds=te, truncateds=tr, bootstrap_values=bv)
     out = torch.empty_like(r)
     rlscan_returns(r, None, te, tr, bv, out, gamma, 1.0)
     return out
@@ -315,6 +378,7 @@ def _forward(inputs, dones, seed_values, decay, boundary):
     x = _f32("inputs", inputs, (E, T))
     d = _f32("dones", dones, (E, T), dev)
     s = _f32("seed_values", seed_values, (E,), dev, optional=True)
+    _debug_check("forward scan", terminateds=d)
     out = torch.empty_like(x)
     rlscan_prefix(x, d, s, out, decay, boundary)
     return out

@@ -16,7 +16,7 @@ from linear_recurrence_scan_amd import ops
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("rlscan.h", "rlscan_debug.h")]
 
-OK, NULL_ARG, BAD_SHAPE, BAD_PARAM, CONFLICT, WORKSPACE = 0, 1, 2, 3, 4, 5
+OK, NULL_ARG, BAD_SHAPE, BAD_PARAM, CONFLICT, WORKSPACE, LAUNCH, DATA = 0, 1, 2, 3, 4, 5, 6, 7
 P = ctypes.c_void_p(0x1000)  # fake device pointer, never dereferenced
 N = None
 
@@ -47,8 +47,8 @@ def test_library_exports_every_declared_function(L):
 
 
 def test_abi_version_and_strings(L):
-    assert L.rlscan_abi_version() == 1
-    for st in range(0, 7):
+    assert L.rlscan_abi_version() == 2
+    for st in range(0, 8):
         assert L.rlscan_status_string(st)
     assert L.rlscan_status_string(99) == b"unknown status"
 
@@ -129,6 +129,19 @@ def test_returns_and_prefix_validation(L):
     assert L.rlscan_prefix(P, P, N, N, 4, 8, 1.0, 0, N, 0, N) == NULL_ARG
     assert L.rlscan_prefix(P, P, N, P, 4, 8, 1.0, 7, N, 0, N) == BAD_PARAM
     assert L.rlscan_prefix(P, P, N, P, 4, 8, float("nan"), 0, N, 0, N) == BAD_PARAM
+
+
+def test_check_inputs_validation(L):
+    def call(te=P, tr=N, bv=N, act=N, E=4, T=8, A=0, ws=ctypes.c_void_p(0x100000), nws=1 << 16):
+        return L.rlscan_check_inputs(te, tr, bv, act, E, T, A, ws, nws, N, N)
+    assert call(te=N) == NULL_ARG
+    assert call(E=0) == BAD_SHAPE
+    assert call(T=0) == BAD_SHAPE
+    assert call(act=P, A=0) == BAD_SHAPE
+    assert call(ws=N) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x100040)) == WORKSPACE
+    assert call(nws=1000) == WORKSPACE
+    assert b"workspace" in L.rlscan_last_error()
 
 
 def test_workspace_init_validation(L):

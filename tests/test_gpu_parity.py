@@ -436,3 +436,73 @@ def test_calls_on_one_stream_share_a_workspace_without_clearing():
         outs.append(ops.episodic_prefix_sum(dev(f["inputs"]), dev(f["dones"]), dev(f["seed_values"])))
     for i, o in enumerate(outs):
         assert_close(o, want_r if i % 2 == 0 else want_f, T, f"call {i}")
+
+
+# ---------------------------------------------------------------------------
+# debug data checks (rlscan_check_inputs)
+# ---------------------------------------------------------------------------
+
+def _planted_violations(E, T, seed):
+    """Seeded flags/bootstrap/actions with violations planted at known places;
+    the expected counts come from numpy on the host."""
+    rng = np.random.default_rng(seed)
+    d = synth.gae_inputs(E, T, seed=seed)
+    te, tr, bv = d["terminateds"].copy(), d["truncateds"].copy(), d["bootstrap_values"].copy()
+    A = 18
+    act = rng.integers(0, A, size=(E, T)).astype(np.int64)
+    flat = lambda k: rng.choice(E * T, size=k, replace=False)
+    te.flat[flat(7)] = 0.5                       # not binary
+    tr.flat[flat(3)] = np.nan                    # not binary
+    both = flat(5)
+    te.flat[both], tr.flat[both] = 1.0, 1.0      # both flags
+    bv.flat[flat(11)] = 2.0                      # maybe stray
+    act.flat[flat(4)] = A                        # out of range
+    act.flat[flat(2)] = -1
+    nb = int(np.sum(~np.isin(te, (0.0, 1.0))) + np.sum(~np.isin(tr, (0.0, 1.0))))
+    overlap = int(np.sum((te != 0) & (tr != 0)))
+    interior = np.ones((E, T), bool)
+    interior[:, -1] = False
+    stray = int(np.sum((bv != 0) & (tr == 0) & interior))
+    bad_act = int(np.sum((act < 0) | (act >= A)))
+    return te, tr, bv, act, A, dict(flags_not_binary=nb, term_and_trunc=overlap,
+                                    stray_bootstrap=stray, actions_out_of_range=bad_act)
+
+
+@pytest.mark.parametrize("E,T", [(5, 37), (64, 4099), (3, 200000)])
+def test_check_inputs_counts_planted_violations(E, T):
+    te, tr, bv, act, A, want = _planted_violations(E, T, seed=E * 7 + 1)
+    rep = ops.check_inputs(dev(te), dev(tr), dev(bv), dev(act), A)
+    assert not rep["ok"]
+    for k, v in want.items():
+        assert rep[k] == v, (k, rep[k], v)
+    # a second call on the same workspace starts from zero again
+    rep2 = ops.check_inputs(dev(te), dev(tr), dev(bv), dev(act), A)
+    assert rep2 == rep
+
+
+def test_check_inputs_accepts_the_synthetic_workloads():
+    g = synth.gae_trunc(E=512, T=1024)
+    assert ops.check_inputs(dev(g["terminateds"]), dev(g["truncateds"]),
+                            dev(g["bootstrap_values"]))["ok"]
+    r = synth.retrace_inputs(E=16, T=256, A=18)
+    assert ops.check_inputs(dev(r["terminateds"]), actions=dev(r["actions"]), num_actions=18)["ok"]
+    lr = synth.long_row_inputs(E=4, T=131072)
+    assert ops.check_inputs(dev(lr["dones"]))["ok"]
+
+
+def test_checks_env_switch_guards_the_helpers(monkeypatch):
+    """With RLSCAN_CHECKS=1 a helper refuses bad data; the check leaves the
+    look-back state of the shared workspace intact for the next call."""
+    E, T = 6, 5000
+    d = synth.returns_inputs(E, T, seed=21)
+    bad_te = d["terminateds"].copy()
+    bad_te[2, 17] = 0.25
+    monkeypatch.setenv("RLSCAN_CHECKS", "1")
+    with pytest.raises(ValueError, match="flags_not_binary=1"):
+        ops.discounted_returns(dev(d["rewards"]), dev(bad_te), dev(d["truncateds"]), 0.99,
+                               dev(d["bootstrap_values"]))
+    got = ops.discounted_returns(dev(d["rewards"]), dev(d["terminateds"]), dev(d["truncateds"]),
+                                 0.99, dev(d["bootstrap_values"]))
+    want = oracle.discounted_returns(d["rewards"], d["terminateds"], d["truncateds"], f32(0.99),
+                                     d["bootstrap_values"])
+    assert_close(got, want, T, "after checks")
