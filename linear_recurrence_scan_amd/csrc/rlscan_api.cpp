@@ -72,17 +72,18 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
     const int64_t N = E * T;
     int tile = 0, waves = 0;
     if (!cfg_override(tile, waves)) {
-        // Measured on MI355X (4096 x 1024 GAE): 4 waves x 2 segments per
-        // workgroup is fastest for rows of a few thousand steps; rows of 4096
-        // steps or longer take 4096-element tiles (whole rows per tile, or
-        // fewer look-back hops along a long row); tiny problems take small
-        // tiles so that more workgroups share the work.
+        // Measured on MI355X: 4 waves x 2 segments per workgroup is fastest
+        // for rows of a few thousand steps (4096 x 1024 GAE); rows of 4096
+        // steps or longer take 4096-element tiles of 8 waves x 2 segments
+        // (whole rows per tile, or fewer look-back hops along a long row:
+        // 1024 x 4096 V-trace, 64 x 131072 returns and prefix sums); tiny
+        // problems take small tiles so that more workgroups share the work.
         if (N <= (int64_t)256 * 1024) {
             tile = 256;
             waves = 1;
         } else if (T >= 4096) {
             tile = 4096;
-            waves = 4;
+            waves = 8;
         } else {
             tile = 2048;
             waves = 4;
