@@ -1,7 +1,8 @@
 /*
- * rlscan_debug.h -- diagnostic entry point of librlscan.so (not needed to use
- * the estimators).  It exposes the 64-lane affine wave scan on its own so a
- * test can check the cross-lane data layout of the hardware directly.
+ * rlscan_debug.h -- diagnostic entry points of librlscan.so (not needed to use
+ * the estimators).  They expose the 64-lane affine wave scan on its own, so a
+ * test can check the cross-lane data layout of the hardware directly, and let
+ * a test or a tuning sweep force the launch shape of the scans.
  */
 #ifndef RLSCAN_DEBUG_H
 #define RLSCAN_DEBUG_H
@@ -19,6 +20,16 @@ extern "C" {
  * Errors: NULL pointer -> NULL_ARG; num_waves < 1 or > 65535 -> BAD_SHAPE. */
 rlscan_status rlscan_debug_wave_scan(const float* a, const float* b, float* out_a, float* out_b,
                                      int num_waves, rlscan_stream_t stream);
+
+/* Forces the launch shape of GAE, V-trace, returns and the forward scans for
+ * every later call in the process: `tile` elements per workgroup of `waves`
+ * waves, one of (256, 1), (1024, 2), (2048, 4), (4096, 4), (4096, 8).
+ * (0, 0) restores the planner's choice.  The initial value comes from the
+ * environment variable RLSCAN_CFG="tile,waves" when it names one of these.
+ * Results do not depend on the shape beyond rounding order.  Process-wide;
+ * set it while no other thread is calling the library.
+ * Errors: any other pair -> BAD_PARAM. */
+rlscan_status rlscan_debug_set_launch_shape(int tile, int waves);
 
 #ifdef __cplusplus
 }

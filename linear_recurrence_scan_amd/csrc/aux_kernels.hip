@@ -1,6 +1,9 @@
 // aux_kernels.hip -- small kernels around the estimator scans: workspace
 // fill, the debug data checks, and the bare wave-scan primitive exported for
 // layout tests.
+#include <atomic>
+#include <mutex>
+
 #include "rlscan_internal.hpp"
 #include "scan_core.hpp"
 
@@ -67,6 +70,37 @@ rlscan_status launch_check(const float* term, const float* trunc, const float* b
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
     return RLSCAN_OK;
+}
+
+int resident_workgroups(const void* kernel, int threads) {
+    // Small fixed cache: (kernel, device) -> workgroups resident at once.
+    struct Entry {
+        const void* kernel;
+        int device;
+        int count;
+    };
+    static Entry cache[256];
+    static std::atomic<int> used{0};
+    static std::mutex mu;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const int n = used.load(std::memory_order_acquire);
+    for (int i = 0; i < n; ++i)
+        if (cache[i].kernel == kernel && cache[i].device == dev) return cache[i].count;
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;  // unknown: treated as "not resident at once"
+    }
+    const int count = per_cu * cus;
+    std::lock_guard<std::mutex> lock(mu);
+    const int m = used.load(std::memory_order_relaxed);
+    if (m < 256) {
+        cache[m] = Entry{kernel, dev, count};
+        used.store(m + 1, std::memory_order_release);
+    }
+    return count;
 }
 
 rlscan_status launch_fill_zero(void* p, size_t bytes, hipStream_t s) {

@@ -2,6 +2,7 @@
 // only, before any HIP call), launch planning, and dispatch to the kernels.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -16,26 +17,34 @@ thread_local char g_last_error[512] = "";
 
 bool aligned16(const void* p) { return p == nullptr || (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Launch-shape override for tuning experiments: RLSCAN_CFG="tile,waves" with
-// one of 256,1 / 2048,4 / 4096,4 / 4096,8.
-bool cfg_override(int& tile, int& waves) {
-    static int cached_tile = -1, cached_waves = 0;
-    if (cached_tile < 0) {
-        cached_tile = 0;
+// Launch-shape override of the four-elements-per-lane ops: set by
+// rlscan_debug_set_launch_shape, initially from RLSCAN_CFG="tile,waves".
+// Tile 0 means the planner's choice.
+bool known_shape(int t, int w) {
+    return (t == 256 && w == 1) || (t == 1024 && w == 2) || (t == 2048 && w == 4) ||
+           (t == 4096 && w == 4) || (t == 4096 && w == 8);
+}
+
+std::atomic<int> g_shape{-1};  // tile << 4 | waves; -1 = not read from the environment yet
+
+int forced_shape() {
+    int v = g_shape.load(std::memory_order_relaxed);
+    if (v < 0) {
+        int t = 0, w = 0, init = 0;
         const char* s = std::getenv("RLSCAN_CFG");
-        int t = 0, w = 0;
-        if (s && std::sscanf(s, "%d,%d", &t, &w) == 2) {
-            const bool ok = (t == 256 && w == 1) || (t == 2048 && w == 4) ||
-                            (t == 4096 && w == 4) || (t == 4096 && w == 8);
-            if (ok) {
-                cached_tile = t;
-                cached_waves = w;
-            }
-        }
+        if (s && std::sscanf(s, "%d,%d", &t, &w) == 2 && known_shape(t, w)) init = t << 4 | w;
+        int expected = -1;
+        g_shape.compare_exchange_strong(expected, init, std::memory_order_relaxed);
+        v = g_shape.load(std::memory_order_relaxed);
     }
-    if (cached_tile == 0) return false;
-    tile = cached_tile;
-    waves = cached_waves;
+    return v;
+}
+
+bool cfg_override(int& tile, int& waves) {
+    const int v = forced_shape();
+    if (v <= 0) return false;
+    tile = v >> 4;
+    waves = v & 15;
     return true;
 }
 
@@ -63,6 +72,7 @@ rlscan_status finish_plan(int64_t E, int64_t T, int tile, int waves, bool vec_ok
     plan.geo.vec_ok = vec_ok ? 1 : 0;
     plan.lookback = plan.geo.num_tiles > 1 && (tile % T) != 0;
     plan.geo.interleave = (plan.lookback && E > 1 && T % tile == 0) ? 1 : 0;
+    plan.geo.boost = 0;  // decided per kernel at launch
     if (plan.geo.num_tiles >= kMaxTiles) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
     return RLSCAN_OK;
 }
@@ -72,18 +82,23 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
     const int64_t N = E * T;
     int tile = 0, waves = 0;
     if (!cfg_override(tile, waves)) {
-        // Measured on MI355X: 4 waves x 2 segments per workgroup is fastest
-        // for rows of a few thousand steps (4096 x 1024 GAE); rows of 4096
-        // steps or longer take 4096-element tiles of 8 waves x 2 segments
-        // (whole rows per tile, or fewer look-back hops along a long row:
-        // 1024 x 4096 V-trace, 64 x 131072 returns and prefix sums); tiny
-        // problems take small tiles so that more workgroups share the work.
+        // Measured on MI355X.  Tiny problems take small tiles so that more
+        // workgroups share the work.  Rows of 4096 steps or longer take
+        // 4096-element tiles of 8 waves x 2 segments (whole rows per tile, or
+        // fewer look-back hops along a long row: 1024 x 4096 V-trace,
+        // 64 x 131072 returns and prefix sums).  Rows that divide 1024 take
+        // 1024-element tiles of 2 waves x 2 segments, which need no
+        // look-back (4096 x 1024 GAE: 1% faster than 2048-element tiles).
+        // Other rows take 2048-element tiles of 4 waves x 2 segments.
         if (N <= (int64_t)256 * 1024) {
             tile = 256;
             waves = 1;
         } else if (T >= 4096) {
             tile = 4096;
             waves = 8;
+        } else if (1024 % T == 0) {
+            tile = 1024;
+            waves = 2;
         } else {
             tile = 2048;
             waves = 4;
@@ -349,6 +364,17 @@ rlscan_status rlscan_prefix(const float* inputs, const float* dones, const float
     RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
     PrefixArgs a{inputs, dones, seed, out, decay, boundary == RLSCAN_STARTS_AT ? 1 : 0};
     return launch_prefix(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+rlscan_status rlscan_debug_set_launch_shape(int tile, int waves) {
+    if (tile == 0 && waves == 0) {
+        g_shape.store(0, std::memory_order_relaxed);
+        return RLSCAN_OK;
+    }
+    if (!known_shape(tile, waves))
+        return set_error(RLSCAN_ERR_BAD_PARAM, "unknown launch shape (see rlscan_debug.h)");
+    g_shape.store(tile << 4 | waves, std::memory_order_relaxed);
+    return RLSCAN_OK;
 }
 
 rlscan_status rlscan_debug_wave_scan(const float* a, const float* b, float* out_a, float* out_b,

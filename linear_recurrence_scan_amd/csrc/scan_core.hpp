@@ -114,6 +114,7 @@ struct Geo {
     uint32_t magic;     // floor((2^32-1)/T) when T < tile, for the small-T division
     int vec_ok;         // every [E,T] pointer is 16-byte aligned
     int interleave;     // rows are whole multiples of the tile and tiles run column-major
+    int boost;          // the whole grid is resident at once: issue loads at raised priority
 };
 
 // Quotient of x / T for x < 2^31 using a precomputed reciprocal; exact after

@@ -98,7 +98,14 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
         return make_grp<G, BACKWARD, FAST>(g, tl, off);
     };
 
-    // phase 1: issue every load of every segment
+    // phase 1: issue every load of every segment.  When the whole grid is
+    // resident at once (one round of workgroups), the waves issue their loads
+    // at raised priority, so every wave's requests reach the memory system
+    // before any wave spends issue slots on arithmetic: 1.5-2% faster on
+    // 4096 x 1024 GAE.  With several rounds the same hint lets newly started
+    // workgroups starve the epilogues of older ones, which then hold their
+    // slots longer, so it stays off there.
+    if (g.boost) __builtin_amdgcn_s_setprio(3);
     Raw raw[SEGS];
     uint32_t edges[SEGS];
 #pragma unroll
@@ -107,6 +114,8 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
         edges[s] = gr.edges;
         op.template load<FAST>(g, tl, seg_info(s), gr, raw[s]);
     }
+
+    if (g.boost) __builtin_amdgcn_s_setprio(0);
 
     // A tile whose first scan element starts a row segment needs no carry.
     bool need_carry = false;
@@ -254,16 +263,26 @@ __attribute__((amdgpu_waves_per_eu(WavesPerEu<Op, SEGS, LOOKBACK>::value))) void
         scan_tile<Op, WAVES, SEGS, LOOKBACK, false>(op, g, tl, ws, q, stride, ticket, sh, lds_wave);
 }
 
+// Workgroups of `kernel` (no dynamic LDS) that one device holds at once:
+// occupancy per CU times the CU count, cached per kernel and device.
+int resident_workgroups(const void* kernel, int threads);
+
+template <class Op, int WAVES, int SEGS, bool LOOKBACK>
+rlscan_status launch_one(const Op& op, Geo g, void* ws, size_t lds_bytes, hipStream_t stream) {
+    const void* k = reinterpret_cast<const void*>(&scan_kernel<Op, WAVES, SEGS, LOOKBACK>);
+    g.boost = (lds_bytes == 0 && g.num_tiles <= resident_workgroups(k, WAVES * kWave)) ? 1 : 0;
+    hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, LOOKBACK>), dim3((unsigned)g.num_tiles),
+                       dim3(WAVES * kWave), lds_bytes, stream, op, g, static_cast<uint8_t*>(ws));
+    return RLSCAN_OK;
+}
+
 template <class Op, int WAVES, int SEGS>
 rlscan_status launch_cfg(const Op& op, const Geo& g, bool lookback, void* ws, size_t lds_bytes,
                          hipStream_t stream) {
-    const dim3 grid((unsigned)g.num_tiles), block(WAVES * kWave);
-    if (lookback)
-        hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, true>), grid, block, lds_bytes, stream, op,
-                           g, static_cast<uint8_t*>(ws));
-    else
-        hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, false>), grid, block, lds_bytes, stream, op,
-                           g, static_cast<uint8_t*>(ws));
+    const rlscan_status st = lookback
+                                 ? launch_one<Op, WAVES, SEGS, true>(op, g, ws, lds_bytes, stream)
+                                 : launch_one<Op, WAVES, SEGS, false>(op, g, ws, lds_bytes, stream);
+    if (st != RLSCAN_OK) return st;
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
     return RLSCAN_OK;
@@ -274,6 +293,7 @@ template <class Op>
 rlscan_status launch_g4(const Op& op, const Plan& plan, void* ws, hipStream_t stream) {
     const int w = plan.waves, t = plan.tile;
     if (t == 256 && w == 1) return launch_cfg<Op, 1, 1>(op, plan.geo, plan.lookback, ws, 0, stream);
+    if (t == 1024 && w == 2) return launch_cfg<Op, 2, 2>(op, plan.geo, plan.lookback, ws, 0, stream);
     if (t == 2048 && w == 4) return launch_cfg<Op, 4, 2>(op, plan.geo, plan.lookback, ws, 0, stream);
     if (t == 4096 && w == 4) return launch_cfg<Op, 4, 4>(op, plan.geo, plan.lookback, ws, 0, stream);
     if (t == 4096 && w == 8) return launch_cfg<Op, 8, 2>(op, plan.geo, plan.lookback, ws, 0, stream);

@@ -80,11 +80,12 @@ def _declare(L):
     L.rlscan_returns.argtypes = [vp] * 6 + [i64, i64, f32, f32, vp, sz, vp]
     L.rlscan_prefix.argtypes = [vp] * 4 + [i64, i64, f32, ctypes.c_int, vp, sz, vp]
     L.rlscan_debug_wave_scan.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
+    L.rlscan_debug_set_launch_shape.argtypes = [ctypes.c_int, ctypes.c_int]
     L.rlscan_check_inputs.argtypes = [vp] * 4 + [i64, i64, i64, vp, sz,
                                                  ctypes.POINTER(CheckReport), vp]
     for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
                  "rlscan_gae", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
-                 "rlscan_check_inputs"):
+                 "rlscan_check_inputs", "rlscan_debug_set_launch_shape"):
         getattr(L, name).restype = st
     return L
 
@@ -261,6 +262,15 @@ def rlscan_prefix(inputs, dones, seed, out, decay, boundary):
     st = lib().rlscan_prefix(_ptr(inputs), _ptr(dones), _ptr(seed), _ptr(out), E, T, float(decay),
                              int(b), _ptr(ws), nws, _stream(dev))
     _check("rlscan_prefix", st)
+
+
+LAUNCH_SHAPES = ((256, 1), (1024, 2), (2048, 4), (4096, 4), (4096, 8))
+
+
+def set_launch_shape(tile=0, waves=0):
+    """Forces the launch shape of the four-elements-per-lane scans ((0, 0):
+    the planner's choice); see include/rlscan_debug.h."""
+    _check("rlscan_debug_set_launch_shape", lib().rlscan_debug_set_launch_shape(int(tile), int(waves)))
 
 
 def rlscan_debug_wave_scan(a, b, out_a, out_b):

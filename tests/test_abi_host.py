@@ -144,6 +144,14 @@ def test_check_inputs_validation(L):
     assert b"workspace" in L.rlscan_last_error()
 
 
+def test_launch_shape_override_validation(L):
+    assert L.rlscan_debug_set_launch_shape(1024, 3) == BAD_PARAM
+    assert L.rlscan_debug_set_launch_shape(512, 1) == BAD_PARAM
+    for t, w in ops.LAUNCH_SHAPES:
+        assert L.rlscan_debug_set_launch_shape(t, w) == OK
+    assert L.rlscan_debug_set_launch_shape(0, 0) == OK
+
+
 def test_workspace_init_validation(L):
     assert L.rlscan_workspace_init(N, 4096, N) == NULL_ARG
     assert L.rlscan_workspace_init(ctypes.c_void_p(0x1010), 4096, N) == WORKSPACE

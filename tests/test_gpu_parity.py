@@ -506,3 +506,53 @@ def test_checks_env_switch_guards_the_helpers(monkeypatch):
     want = oracle.discounted_returns(d["rewards"], d["terminateds"], d["truncateds"], f32(0.99),
                                      d["bootstrap_values"])
     assert_close(got, want, T, "after checks")
+
+
+# ---------------------------------------------------------------------------
+# every compiled launch shape (the planner picks only some of them by default)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", ops.LAUNCH_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_every_launch_shape_matches_the_oracle(shape):
+    """Each shape on rows that straddle tiles, rows spanning many tiles with a
+    ragged tail, and whole-tile rows (the column-major look-back order)."""
+    ops.set_launch_shape(*shape)
+    try:
+        for E, T in ((7, 1000), (3, 9001), (6, 8192), (64, 1024)):
+            seed = E * 131 + T
+            g = synth.gae_inputs(E, T, seed=seed)
+            adv, ret = ops.gae(dev(g["rewards"]), dev(g["values"]), dev(g["terminateds"]),
+                               dev(g["truncateds"]), 0.99, 0.95, dev(g["bootstrap_values"]),
+                               want_returns=True)
+            want_adv, want_ret = oracle.gae(g["rewards"], g["values"], g["terminateds"],
+                                            g["truncateds"], f32(0.99), f32(0.95),
+                                            g["bootstrap_values"])
+            assert_close(adv, want_adv, T, f"gae {shape} {E}x{T}")
+            assert_close(ret, want_ret, T, f"gae returns {shape} {E}x{T}")
+
+            v = synth.vtrace_inputs(E, T, seed=seed + 1, two_logprobs=True, p_trunc=0.002,
+                                    boot="2d")
+            vs, pg = ops.vtrace(dev(v["log_pi_target"]), dev(v["log_pi_behavior"]),
+                                dev(v["values"]), dev(v["rewards"]), dev(v["terminateds"]),
+                                dev(v["truncateds"]), 0.99, 1.0, 1.0, dev(v["bootstrap_values"]))
+            want_vs, want_pg = oracle.vtrace(v["log_pi_target"], v["log_pi_behavior"], v["values"],
+                                             v["rewards"], v["terminateds"], v["truncateds"],
+                                             f32(0.99), f32(1.0), f32(1.0), v["bootstrap_values"])
+            assert_close(vs, want_vs, T, f"vtrace vs {shape} {E}x{T}")
+            assert_close(pg, want_pg, T, f"vtrace pg {shape} {E}x{T}")
+
+            r = synth.returns_inputs(E, T, seed=seed + 2)
+            got = ops.lambda_returns(dev(r["rewards"]), dev(r["next_values"]), dev(r["terminateds"]),
+                                     dev(r["truncateds"]), 0.99, 0.9, dev(r["bootstrap_values"]))
+            want = oracle.lambda_returns(r["rewards"], r["next_values"], r["terminateds"],
+                                         r["truncateds"], f32(0.99), f32(0.9), r["bootstrap_values"])
+            assert_close(got, want, T, f"lambda returns {shape} {E}x{T}")
+
+            f = synth.forward_inputs(E, T, seed=seed + 3)
+            for boundary in ("ends_at", "starts_at"):
+                got = ops.episodic_prefix_sum(dev(f["inputs"]), dev(f["dones"]),
+                                              dev(f["seed_values"]), boundary)
+                want = oracle.forward_scan(f["inputs"], f["dones"], f["seed_values"], 1.0, boundary)
+                assert_close(got, want, T, f"prefix {boundary} {shape} {E}x{T}")
+    finally:
+        ops.set_launch_shape(0, 0)
