@@ -2,7 +2,8 @@
  * rlscan_debug.h -- diagnostic entry points of librlscan.so (not needed to use
  * the estimators).  They expose the 64-lane affine wave scan on its own, so a
  * test can check the cross-lane data layout of the hardware directly, and let
- * a test or a tuning sweep force the launch shape of the scans.
+ * a test or a tuning sweep force the launch shape of the scans or scramble the
+ * timing of the cross-workgroup carry propagation.
  */
 #ifndef RLSCAN_DEBUG_H
 #define RLSCAN_DEBUG_H
@@ -30,6 +31,15 @@ rlscan_status rlscan_debug_wave_scan(const float* a, const float* b, float* out_
  * set it while no other thread is calling the library.
  * Errors: any other pair -> BAD_PARAM. */
 rlscan_status rlscan_debug_set_launch_shape(int tile, int waves);
+
+/* Look-back stress switch: with a nonzero `seed`, every later call whose rows
+ * span tiles delays each tile by a bounded pseudo-random time (up to about
+ * 6 microseconds, a function of the seed and the tile) before it publishes
+ * its partial results, so tiles finish in an order unrelated to their launch
+ * order.  Results must not change: every carry is the same fixed function of
+ * the inputs whatever the timing.  0 turns it off.  Process-wide; set it
+ * while no other thread is calling the library.  Always returns RLSCAN_OK. */
+rlscan_status rlscan_debug_set_lookback_jitter(uint32_t seed);
 
 #ifdef __cplusplus
 }

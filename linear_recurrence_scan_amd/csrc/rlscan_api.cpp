@@ -25,6 +25,7 @@ bool known_shape(int t, int w) {
            (t == 4096 && w == 4) || (t == 4096 && w == 8);
 }
 
+std::atomic<uint32_t> g_jitter{0};  // look-back stress delay seed (0 = off)
 std::atomic<int> g_shape{-1};  // tile << 4 | waves; -1 = not read from the environment yet
 
 int forced_shape() {
@@ -73,6 +74,7 @@ rlscan_status finish_plan(int64_t E, int64_t T, int tile, int waves, bool vec_ok
     plan.lookback = plan.geo.num_tiles > 1 && (tile % T) != 0;
     plan.geo.interleave = (plan.lookback && E > 1 && T % tile == 0) ? 1 : 0;
     plan.geo.boost = 0;  // decided per kernel at launch
+    plan.geo.jitter = g_jitter.load(std::memory_order_relaxed);
     if (plan.geo.num_tiles >= kMaxTiles) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
     return RLSCAN_OK;
 }
@@ -364,6 +366,11 @@ rlscan_status rlscan_prefix(const float* inputs, const float* dones, const float
     RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
     PrefixArgs a{inputs, dones, seed, out, decay, boundary == RLSCAN_STARTS_AT ? 1 : 0};
     return launch_prefix(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+rlscan_status rlscan_debug_set_lookback_jitter(uint32_t seed) {
+    g_jitter.store(seed, std::memory_order_relaxed);
+    return RLSCAN_OK;
 }
 
 rlscan_status rlscan_debug_set_launch_shape(int tile, int waves) {

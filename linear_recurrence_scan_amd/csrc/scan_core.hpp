@@ -115,6 +115,7 @@ struct Geo {
     int vec_ok;         // every [E,T] pointer is 16-byte aligned
     int interleave;     // rows are whole multiples of the tile and tiles run column-major
     int boost;          // the whole grid is resident at once: issue loads at raised priority
+    uint32_t jitter;    // nonzero: look-back stress test, seeded delay before each publication
 };
 
 // Quotient of x / T for x < 2^31 using a precomputed reciprocal; exact after
@@ -402,8 +403,22 @@ __device__ __forceinline__ bool lookback_resolve(const LookbackView& v, uint32_t
 // value, and a tile publishes its inclusive value only once), so results are
 // bitwise reproducible.  Waits are bounded: past kSpinLimit polls the error
 // word is set and the tile proceeds with a zero carry.
+// Stress-test delay (debug only): a bounded pseudo-random wait of 0 to 7
+// sleeps of 2048 cycles (up to about 6 microseconds), different per tile and
+// per seed, so that tiles publish in an order unrelated to their launch order.
+__device__ __forceinline__ void jitter_delay(uint32_t seed, int64_t q) {
+    uint32_t h = seed ^ (uint32_t)q * 0x9E3779B9u;
+    h ^= h >> 16;
+    h *= 0x85EBCA6Bu;
+    h ^= h >> 13;
+    const uint32_t n = h & 7u;
+    for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(32);
+}
+
 __device__ __forceinline__ float lookback(uint8_t* ws, uint32_t epoch, int64_t q, int64_t stride,
-                                          Affine tot, bool need_carry, uint64_t early) {
+                                          Affine tot, bool need_carry, uint64_t early,
+                                          uint32_t jitter = 0) {
+    if (jitter) jitter_delay(jitter, q);
     uint64_t* slots = reinterpret_cast<uint64_t*>(ws + WsHeader::kSlotsByteOffset);
     uint32_t* hdr = reinterpret_cast<uint32_t*>(ws);
     const uint32_t tag_agg = 2u * epoch + 1u;

@@ -179,7 +179,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
         if (wave == 0) {
             const uint64_t t = readfirstlane_u64(ticket);
             if (lane == 0) epoch_advance(ws, q, g.num_tiles, t);
-            x = lookback(ws, (uint32_t)(t >> 32), q, stride, ttot, need_carry, early);
+            x = lookback(ws, (uint32_t)(t >> 32), q, stride, ttot, need_carry, early, g.jitter);
         }
         if constexpr (WAVES > 1) {
             if (threadIdx.x == 0) sh.carry = x;

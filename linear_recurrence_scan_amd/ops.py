@@ -81,11 +81,13 @@ def _declare(L):
     L.rlscan_prefix.argtypes = [vp] * 4 + [i64, i64, f32, ctypes.c_int, vp, sz, vp]
     L.rlscan_debug_wave_scan.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
     L.rlscan_debug_set_launch_shape.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.rlscan_debug_set_lookback_jitter.argtypes = [ctypes.c_uint32]
     L.rlscan_check_inputs.argtypes = [vp] * 4 + [i64, i64, i64, vp, sz,
                                                  ctypes.POINTER(CheckReport), vp]
     for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
                  "rlscan_gae", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
-                 "rlscan_check_inputs", "rlscan_debug_set_launch_shape"):
+                 "rlscan_check_inputs", "rlscan_debug_set_launch_shape",
+                 "rlscan_debug_set_lookback_jitter"):
         getattr(L, name).restype = st
     return L
 
@@ -271,6 +273,11 @@ def set_launch_shape(tile=0, waves=0):
     """Forces the launch shape of the four-elements-per-lane scans ((0, 0):
     the planner's choice); see include/rlscan_debug.h."""
     _check("rlscan_debug_set_launch_shape", lib().rlscan_debug_set_launch_shape(int(tile), int(waves)))
+
+
+def set_lookback_jitter(seed=0):
+    """Look-back stress switch (0 = off); see include/rlscan_debug.h."""
+    _check("rlscan_debug_set_lookback_jitter", lib().rlscan_debug_set_lookback_jitter(int(seed)))
 
 
 def rlscan_debug_wave_scan(a, b, out_a, out_b):

@@ -556,3 +556,39 @@ def test_every_launch_shape_matches_the_oracle(shape):
                 assert_close(got, want, T, f"prefix {boundary} {shape} {E}x{T}")
     finally:
         ops.set_launch_shape(0, 0)
+
+
+# ---------------------------------------------------------------------------
+# look-back under scrambled timing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [1, 0xBEEF, 0x12345678])
+def test_lookback_results_do_not_depend_on_timing(seed):
+    """Tiles delayed by seeded pseudo-random times before they publish give
+    bitwise the same results as undelayed ones: row-major tiles over rows that
+    straddle tiles, column-major tiles over whole-tile rows, both directions,
+    and Retrace's 1024-step tiles."""
+    cases = []
+    r = synth.returns_inputs(5, 20011, seed=seed % 1000 + 7)
+    cases.append(lambda: ops.lambda_returns(dev(r["rewards"]), dev(r["next_values"]),
+                                            dev(r["terminateds"]), dev(r["truncateds"]), 0.999,
+                                            0.97, dev(r["bootstrap_values"])))
+    g = synth.gae_inputs(300, 1000, seed=seed % 1000 + 8)
+    cases.append(lambda: ops.gae(dev(g["rewards"]), dev(g["values"]), dev(g["terminateds"]),
+                                 dev(g["truncateds"]), 0.99, 0.95, dev(g["bootstrap_values"])))
+    f = synth.forward_inputs(16, 65536, seed=seed % 1000 + 9)
+    cases.append(lambda: ops.episodic_prefix_sum(dev(f["inputs"]), dev(f["dones"]),
+                                                 dev(f["seed_values"]), "ends_at"))
+    d = synth.retrace_inputs(E=24, T=4096, A=7, seed=seed % 1000 + 10)
+    cases.append(lambda: ops.retrace(dev(d["pi_target"]), dev(d["mu_taken"]), dev(d["q_taken"]),
+                                     dev(d["next_q_all"]), dev(d["actions"]), dev(d["rewards"]),
+                                     dev(d["terminateds"]), None, 0.99, 0.95)[0])
+    plain = [host(c()) for c in cases]
+    ops.set_lookback_jitter(seed)
+    try:
+        for _ in range(2):
+            for c, want in zip(cases, plain):
+                np.testing.assert_array_equal(host(c()), want)
+    finally:
+        ops.set_lookback_jitter(0)
+    assert ops.workspace_error() == 0
