@@ -11,23 +11,42 @@
 
 namespace rlscan {
 
-// One element per lane (G = 1).  A segment's slab of
-// 64*A floats of pi_target and next_q_all is read once with contiguous
-// float4 loads, staged in LDS (pi and pi*Q), and each lane then reduces its
-// own step's A entries and gathers pi[t, a_t].  c_{t+1} and q_{t+1} come
-// from the neighbouring lane (Retrace page, Sec. 5: the shifted trace weight
+// One element per lane (G = 1).  A segment's slab of 64*A floats of
+// pi_target and next_q_all is read with contiguous 16-byte loads, staged in
+// this wave's own LDS region (pi and pi*Q), and each lane then reduces its
+// own step's A entries and gathers pi[t, a_t].  c_{t+1} and q_{t+1} come from
+// the neighbouring lane (Retrace page, Sec. 5: the shifted trace weight
 // without a second read of the 3-D tensor).
 //   adv_t = u_t + k_t Delta_{t+1},  u_t = rho_t (r_t - q_t + gamma (1-term_t) q_{t+1}),
 //   k_t = rho_t gamma (1-term_t); at the row end u = rho (r - q), k = 0.
+//
+// KMAX > 0 (A <= 4*KMAX): in whole, aligned tiles every segment's slab is
+// loaded into registers (KMAX 16-byte pieces of each array per lane) in the
+// load phase, together with everything else the tile reads, so a wave has
+// all its reads in flight at once; the LDS staging then only moves data
+// already on chip.  KMAX = 0, or a partial tile, loads each segment's slab
+// when the segment is staged.
+
+// Orders this wave's LDS accesses: the staging region is private to the wave,
+// so no workgroup barrier is needed, only that no lane's access moves across.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int KMAX>
 struct RetraceOp {
     static constexpr int G = 1;
     static constexpr bool BACKWARD = true;
     static constexpr bool kFits64 = false;
+    static constexpr int kSlab = KMAX > 0 ? KMAX : 1;
     RetraceArgs p;
     struct Raw {
         float mu, q, r, te, tr;
         int64_t act;
         float c_h, q_h;  // halo: c and q of the scan-previous element (lane 0)
+        f32x4 pi4[kSlab], qn4[kSlab];  // 16-byte pieces lane + 64*k of the segment's slab
     };
     struct Keep {
         float q, u, k;
@@ -41,6 +60,20 @@ struct RetraceOp {
                          Raw& w) const {
         const bool valid = bit(gr.valid, 0);
         const int64_t f = tl.lo + gr.off;
+        if constexpr (FAST && KMAX > 0) {
+            // whole segment in range and 16-byte aligned: 16*A pieces per array
+            const int lane = lane_id();
+            const int n4 = 16 * (int)p.A;
+            const int64_t slab = si.seg_lo * p.A;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                const int i = lane + kWave * k;
+                if (i < n4) {
+                    w.pi4[k] = load16(p.pi_target + slab + 4 * i);
+                    w.qn4[k] = load16(p.next_q_all + slab + 4 * i);
+                }
+            }
+        }
         w.mu = valid ? p.mu_taken[f] : 1.f;
         w.q = valid ? p.q_taken[f] : 0.f;
         w.r = valid ? p.rewards[f] : 0.f;
@@ -57,43 +90,51 @@ struct RetraceOp {
         }
     }
 
-    // Stages the segment's pi and pi*Q slab in LDS and returns E_t and pi[t,a_t]
-    // for this lane's step.  Called by every lane of the workgroup.
+    // Stages the segment's pi and pi*Q slab in this wave's LDS region and
+    // returns E_t and pi[t,a_t] for this lane's step.  Called by every lane
+    // of the wave.
+    template <bool FAST>
     __device__ void expectation(const Geo& g, const Tile& tl, const SegInfo& si, const Grp& gr,
                                 const Raw& w, float& expect, float& pia) const {
         const int lane = lane_id();
         const int A = (int)p.A;
         float* lpi = si.lds;
         float* lprod = si.lds + kWave * A;
-        const int64_t nvalid64 = g.N - si.seg_lo;
-        const int nvalid = nvalid64 >= kWave ? kWave : (nvalid64 > 0 ? (int)nvalid64 : 0);
-        const int nflt = nvalid * A;
-        const int64_t slab = si.seg_lo * p.A;
-        __syncthreads();  // previous segment's LDS reads are done
-        if (g.vec_ok) {
-            const int n4 = nflt >> 2;
-            const float4* pi4 = reinterpret_cast<const float4*>(p.pi_target + slab);
-            const float4* qn4 = reinterpret_cast<const float4*>(p.next_q_all + slab);
-            for (int i = lane; i < n4; i += kWave) {
-                const float4 a = pi4[i];
-                const float4 b = qn4[i];
-                reinterpret_cast<float4*>(lpi)[i] = a;
-                reinterpret_cast<float4*>(lprod)[i] =
-                    make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
-            }
-            for (int i = (n4 << 2) + lane; i < nflt; i += kWave) {
-                const float a = p.pi_target[slab + i];
-                lpi[i] = a;
-                lprod[i] = a * p.next_q_all[slab + i];
+        wave_lds_sync();  // this wave's reads of the previous segment are done
+        if constexpr (FAST && KMAX > 0) {
+            const int n4 = 16 * A;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k) {
+                const int i = lane + kWave * k;
+                if (i < n4) {
+                    const f32x4 a = w.pi4[k];
+                    reinterpret_cast<f32x4*>(lpi)[i] = a;
+                    reinterpret_cast<f32x4*>(lprod)[i] = a * w.qn4[k];
+                }
             }
         } else {
-            for (int i = lane; i < nflt; i += kWave) {
+            const int64_t nvalid64 = g.N - si.seg_lo;
+            const int nvalid = nvalid64 >= kWave ? kWave : (nvalid64 > 0 ? (int)nvalid64 : 0);
+            const int nflt = nvalid * A;
+            const int64_t slab = si.seg_lo * p.A;
+            int done = 0;
+            if (g.vec_ok) {
+                const int n4 = nflt >> 2;
+                for (int i = lane; i < n4; i += kWave) {
+                    const f32x4 a = load16(p.pi_target + slab + 4 * i);
+                    const f32x4 b = load16(p.next_q_all + slab + 4 * i);
+                    reinterpret_cast<f32x4*>(lpi)[i] = a;
+                    reinterpret_cast<f32x4*>(lprod)[i] = a * b;
+                }
+                done = n4 << 2;
+            }
+            for (int i = done + lane; i < nflt; i += kWave) {
                 const float a = p.pi_target[slab + i];
                 lpi[i] = a;
                 lprod[i] = a * p.next_q_all[slab + i];
             }
         }
-        __syncthreads();
+        wave_lds_sync();
         expect = 0.f;
         pia = 0.f;
         if (bit(gr.valid, 0)) {
@@ -133,22 +174,45 @@ struct RetraceOp {
     }
 };
 
-template <>
-struct IsStaged<RetraceOp> {
+template <int KMAX>
+struct IsStaged<RetraceOp<KMAX>> {
     static constexpr bool value = true;
 };
 
-rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s) {
-    RetraceOp op;
+template <int KMAX>
+static rlscan_status launch(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s) {
+    RetraceOp<KMAX> op;
     op.p = a;
     const size_t lds = (size_t)plan.waves * 2 * kWave * (size_t)a.A * sizeof(float);
-    if (plan.waves == 4 && plan.tile == 1024)
-        return launch_cfg<RetraceOp, 4, 4>(op, plan.geo, plan.lookback, ws, lds, s);
-    if (plan.waves == 1 && plan.tile == 1024)
-        return launch_cfg<RetraceOp, 1, 16>(op, plan.geo, plan.lookback, ws, lds, s);
-    if (plan.waves == 1 && plan.tile == 256)
-        return launch_cfg<RetraceOp, 1, 4>(op, plan.geo, plan.lookback, ws, lds, s);
+    const int t = plan.tile, w = plan.waves;
+    if constexpr (KMAX > 0) {
+        if (t == 1024 && w == 8)
+            return launch_cfg<RetraceOp<KMAX>, 8, 2>(op, plan.geo, plan.lookback, ws, lds, s);
+        if (t == 512 && w == 4)
+            return launch_cfg<RetraceOp<KMAX>, 4, 2>(op, plan.geo, plan.lookback, ws, lds, s);
+    } else {
+        if (t == 1024 && w == 4)
+            return launch_cfg<RetraceOp<KMAX>, 4, 4>(op, plan.geo, plan.lookback, ws, lds, s);
+        if (t == 1024 && w == 1)
+            return launch_cfg<RetraceOp<KMAX>, 1, 16>(op, plan.geo, plan.lookback, ws, lds, s);
+        if (t == 256 && w == 1)
+            return launch_cfg<RetraceOp<KMAX>, 1, 4>(op, plan.geo, plan.lookback, ws, lds, s);
+    }
     return set_error(RLSCAN_ERR_BAD_PARAM, "internal: unsupported retrace tile");
+}
+
+// Register budget for the slab pieces by action count: 5 pieces per array
+// and lane up to A = 20, 8 up to A = 32; wider action sets stage each
+// segment's slab when they reach it.
+int retrace_pieces(int64_t A) { return A <= 20 ? 5 : (A <= 32 ? 8 : 0); }
+
+rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s) {
+    if (plan.tile == 256) return launch<0>(a, plan, ws, s);  // small problems: short registers
+    switch (retrace_pieces(a.A)) {
+        case 5: return launch<5>(a, plan, ws, s);
+        case 8: return launch<8>(a, plan, ws, s);
+        default: return launch<0>(a, plan, ws, s);
+    }
 }
 
 }  // namespace rlscan

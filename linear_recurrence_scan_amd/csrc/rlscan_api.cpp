@@ -111,11 +111,16 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
 
 rlscan_status plan_retrace(int64_t E, int64_t T, int64_t A, Plan& plan, bool vec_ok) {
     const int64_t N = E * T;
-    int tile = 1024, waves = 4;
-    if (A > 32) waves = 1;  // 2*64*A floats of LDS per wave
+    int tile, waves;
     if (N <= (int64_t)64 * 1024) {
-        tile = 256;
+        tile = 256;  // small problems: many one-wave workgroups
         waves = 1;
+    } else if (retrace_pieces(A) > 0) {
+        tile = 1024;  // 8 waves x 2 segments, slabs loaded up front
+        waves = 8;
+    } else {
+        tile = 1024;  // 2*64*A floats of LDS per wave: one wave per workgroup
+        waves = A > 32 ? 1 : 4;
     }
     return finish_plan(E, T, tile, waves, vec_ok, plan);
 }

@@ -60,6 +60,9 @@ rlscan_status set_error(rlscan_status st, const char* msg);
 rlscan_status launch_gae(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_vtrace(const VtraceArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s);
+// 16-byte pieces of each 3-D array a lane holds per segment for A actions (0:
+// each segment's slab is loaded when it is staged).
+int retrace_pieces(int64_t A);
 rlscan_status launch_returns(const ReturnsArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_prefix(const PrefixArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_fill_zero(void* p, size_t bytes, hipStream_t s);

@@ -139,7 +139,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
         gr.edges = edges[s];
         if constexpr (IsStaged<Op>::value) {
             float expect, pia;
-            op.expectation(g, tl, seg_info(s), gr, raw[s], expect, pia);
+            op.template expectation<FAST>(g, tl, seg_info(s), gr, raw[s], expect, pia);
             op.finish(gr, raw[s], expect, pia, al[s], be[s], kp[s]);
         } else {
             op.coeffs(gr, raw[s], al[s], be[s], kp[s]);

@@ -259,6 +259,13 @@ RETRACE_CASES = [
     (4, 1030, 33, 0.01),
     (3, 129, 128, 0.01),
     (64, 64, 7, 0.05),
+    # above 64K steps: 8-wave tiles with the slabs loaded up front (A <= 32)
+    (70, 1000, 18, 0.01),   # rows straddle tiles, ragged last tile
+    (33, 2048, 4, 0.0),     # A = 4: one 16-byte piece per lane and segment
+    (24, 4096, 20, 0.0),    # A = 20: the widest 5-piece case, column-major look-back
+    (20, 4000, 21, 0.01),   # A = 21: 8 pieces per lane
+    (40, 2500, 25, 0.01),
+    (9, 8000, 40, 0.01),    # A > 32: slabs staged per segment
 ]
 
 
@@ -270,6 +277,28 @@ def test_retrace_parity(E, T, A, p_trunc):
     want_q, want_adv = oracle.retrace(*args, f32(0.99), f32(0.95), 1.0, 1.0)
     g = [dev(x) for x in args]
     q, adv = ops.retrace(*g, 0.99, 0.95, 1.0, 1.0)
+    assert_close(q, want_q, T, "q_ret")
+    assert_close(adv, want_adv, T, "advantages")
+
+
+def test_retrace_unaligned_3d_arrays():
+    """3-D arrays that are 4-byte but not 16-byte aligned take the staged
+    per-element path; results are the same."""
+    E, T, A = 40, 2000, 18
+    d = synth.retrace_inputs(E, T, A, seed=77, p_term=0.01)
+    args = (d["pi_target"], d["mu_taken"], d["q_taken"], d["next_q_all"], d["actions"],
+            d["rewards"], d["terminateds"], None)
+    want_q, want_adv = oracle.retrace(*args, f32(0.99), f32(0.95), 1.0, 1.0)
+
+    def shifted(x):
+        buf = torch.empty(x.size + 1, dtype=torch.float32, device="cuda")
+        view = buf[1:].view(x.shape)
+        view.copy_(torch.from_numpy(x))
+        assert view.data_ptr() % 16 != 0
+        return view
+    g = [dev(x) for x in args[:7]]
+    g[0], g[3] = shifted(d["pi_target"]), shifted(d["next_q_all"])
+    q, adv = ops.retrace(*g, None, 0.99, 0.95, 1.0, 1.0)
     assert_close(q, want_q, T, "q_ret")
     assert_close(adv, want_adv, T, "advantages")
 
