@@ -10,16 +10,18 @@ namespace rlscan {
 
 // F: kTrunc (truncateds read), kBoot2D (bootstrap_values read as a full
 // [E,T] array; only with kTrunc).  Without kTrunc the continuation value of a
-// row end comes from last_value or bootstrap_values[:, T-1].
-template <unsigned F>
+// row end comes from last_value or bootstrap_values[:, T-1].  SHORT: rows of
+// fewer than G steps.
+template <unsigned F, bool SHORT>
 struct GaeOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = true;
     static constexpr bool kFits64 = true;
     GaeArgs p;
     struct Raw {
-        float R[G], V[G], TE[G], TR[G], B[G];  // B: continuation value (0 where none)
+        float R[G], V[G], TE[G], TR[G], B[G];  // B: full bootstrap array (kBoot2D)
         float halo;
+        EdgeValue<G, true, SHORT> eb;  // row-end continuation value otherwise
     };
     struct Keep {
         float v;
@@ -39,28 +41,21 @@ struct GaeOp {
             if constexpr ((F & kBoot2D) != 0)
                 load_group<G, true, FAST>(p.bootstrap_values + tl.lo, gr, w.B);
         } else {
-            if ((p.last_value || p.bootstrap_values) && (gr.edges & gr.valid)) {
-#pragma unroll
-                for (int j = 0; j < G; ++j)
-                    if (bit(gr.edges & gr.valid, j)) {
-                        const uint32_t o = gr.off + flat_of_slot<G, true>(j);
-                        w.B[j] = edge_bootstrap(p.last_value, p.bootstrap_values,
-                                                row_at(g, tl, o), tl.lo + o);
-                    }
-            }
+            w.eb.load(g, tl, gr, p.last_value, p.bootstrap_values);
         }
         w.halo = (lane_id() == 0 && si.halo_valid) ? p.values[si.halo_flat] : 0.f;
     }
 
-    __device__ void coeffs(const Grp& gr, const Raw& w, float (&al)[G], float (&be)[G],
-                           Keep (&kp)[G]) const {
+    __device__ void coeffs(const Geo& g, const Tile& tl, const Grp& gr, const Raw& w,
+                           float (&al)[G], float (&be)[G], Keep (&kp)[G]) const {
         float VN[G];
         scan_prev<G>(w.V, w.halo, VN);
         const float gl = p.gamma * p.lambda;
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const bool edge = bit(gr.edges, j);
-            const float b = w.B[j];
+            float b = w.B[j];
+            if constexpr ((F & kTrunc) == 0) b = w.eb.at(gr, j);
             // successor value: bootstrap at the row end, else (1-trunc) V_{t+1} + B_t
             const float vnext = edge ? b : fmaf(1.f - w.TR[j], VN[j], b);
             const float done = fminf(w.TE[j] + w.TR[j], 1.f);
@@ -74,7 +69,7 @@ struct GaeOp {
 
     template <bool FAST>
     __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
-                             const float (&)[G], const Keep (&kp)[G]) const {
+                             const float (&)[G], const float (&)[G], const Keep (&kp)[G]) const {
         store_group<G, true, FAST>(p.advantages + tl.lo, gr, A);
         if (p.returns) {
             float R[G];
@@ -87,7 +82,12 @@ struct GaeOp {
 
 template <unsigned F>
 static rlscan_status launch(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s) {
-    GaeOp<F> op;
+    if (plan.geo.T < 4) {
+        GaeOp<F, true> op;
+        op.p = a;
+        return launch_cfg<GaeOp<F, true>, 4, 2>(op, plan.geo, plan.lookback, ws, 0, s);
+    }
+    GaeOp<F, false> op;
     op.p = a;
     return launch_g4(op, plan, ws, s);
 }

@@ -36,8 +36,8 @@ struct PrefixOp {
         w.halo = (!p.starts_at && lane_id() == 0 && si.halo_valid) ? p.dones[si.halo_flat] : 0.f;
     }
 
-    __device__ void coeffs(const Grp& gr, const Raw& w, float (&al)[G], float (&be)[G],
-                           Keep (&)[G]) const {
+    __device__ void coeffs(const Geo&, const Tile&, const Grp& gr, const Raw& w, float (&al)[G],
+                           float (&be)[G], Keep (&)[G]) const {
         float DP[G];
         scan_prev<G>(w.D, w.halo, DP);
 #pragma unroll
@@ -59,7 +59,7 @@ struct PrefixOp {
 
     template <bool FAST>
     __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
-                             const float (&)[G], const Keep (&)[G]) const {
+                             const float (&)[G], const float (&)[G], const Keep (&)[G]) const {
         store_group<G, false, FAST>(p.out + tl.lo, gr, A);
     }
 };

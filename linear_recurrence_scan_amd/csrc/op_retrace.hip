@@ -165,7 +165,7 @@ struct RetraceOp {
 
     template <bool FAST>
     __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G],
-                             const float (&prevA)[G], const float (&)[G],
+                             const float (&prevA)[G], const float (&)[G], const float (&)[G],
                              const Keep (&kp)[G]) const {
         if (!bit(gr.valid, 0)) return;
         const int64_t f = tl.lo + gr.off;

@@ -11,43 +11,39 @@ namespace rlscan {
 
 // F: kNextValues, kTrunc, kBoot2D (bootstrap_values read as a full array;
 // with kTrunc).  Without kTrunc only column T-1 of bootstrap_values is read,
-// as the row-end carry.
-template <unsigned F>
+// as the row-end carry.  SHORT: rows of fewer than G steps.
+template <unsigned F, bool SHORT>
 struct ReturnsOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = true;
     static constexpr bool kFits64 = true;
     ReturnsArgs p;
     struct Raw {
-        float R[G], TE[G], TR[G], B[G], NV[G], EB[G];  // EB: row-end carry without truncations
+        float R[G], TE[G], TR[G], B[G], NV[G];
+        EdgeValue<G, true, SHORT> eb;  // row-end carry bootstrap_values[:, T-1] without truncations
     };
     struct Keep {};
     __device__ size_t lds_floats_per_wave() const { return 0; }
 
     template <bool FAST>
-    __device__ void load(const Geo&, const Tile& tl, const SegInfo&, const Grp& gr, Raw& w) const {
+    __device__ void load(const Geo& g, const Tile& tl, const SegInfo&, const Grp& gr, Raw& w) const {
         load_group<G, true, FAST>(p.rewards + tl.lo, gr, w.R);
         load_group<G, true, FAST>(p.terminateds + tl.lo, gr, w.TE);
 #pragma unroll
-        for (int j = 0; j < G; ++j) w.TR[j] = w.B[j] = w.NV[j] = w.EB[j] = 0.f;
+        for (int j = 0; j < G; ++j) w.TR[j] = w.B[j] = w.NV[j] = 0.f;
         if constexpr ((F & kTrunc) != 0) {
             load_group<G, true, FAST>(p.truncateds + tl.lo, gr, w.TR);
             if constexpr ((F & kBoot2D) != 0)
                 load_group<G, true, FAST>(p.bootstrap_values + tl.lo, gr, w.B);
         } else {
-            if (p.bootstrap_values && (gr.edges & gr.valid)) {
-#pragma unroll
-                for (int j = 0; j < G; ++j)
-                    if (bit(gr.edges & gr.valid, j))
-                        w.EB[j] = p.bootstrap_values[tl.lo + gr.off + flat_of_slot<G, true>(j)];
-            }
+            w.eb.load(g, tl, gr, nullptr, p.bootstrap_values);
         }
         if constexpr ((F & kNextValues) != 0)
             load_group<G, true, FAST>(p.next_values + tl.lo, gr, w.NV);
     }
 
-    __device__ void coeffs(const Grp& gr, const Raw& w, float (&al)[G], float (&be)[G],
-                           Keep (&)[G]) const {
+    __device__ void coeffs(const Geo& g, const Tile& tl, const Grp& gr, const Raw& w,
+                           float (&al)[G], float (&be)[G], Keep (&)[G]) const {
         constexpr bool kNV = (F & kNextValues) != 0;
         const float lam = kNV ? p.lambda : 1.f;
         const float gl = p.gamma * lam;
@@ -59,7 +55,9 @@ struct ReturnsOp {
             if constexpr (kNV) a = fmaf(g1l * (1.f - done), w.NV[j], a);
             float bb = gl * (1.f - done);
             if (bit(gr.edges, j)) {
-                a = fmaf(bb, w.B[j] + w.EB[j], a);  // carry G_T = B_{T-1}
+                float eb = w.B[j];  // with truncations: the full array's value
+                if constexpr ((F & kTrunc) == 0) eb = w.eb.at(gr, j);
+                a = fmaf(bb, eb, a);  // carry G_T = B_{T-1}
                 bb = 0.f;
             }
             al[j] = bit(gr.valid, j) ? a : 0.f;
@@ -69,14 +67,19 @@ struct ReturnsOp {
 
     template <bool FAST>
     __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
-                             const float (&)[G], const Keep (&)[G]) const {
+                             const float (&)[G], const float (&)[G], const Keep (&)[G]) const {
         store_group<G, true, FAST>(p.out + tl.lo, gr, A);
     }
 };
 
 template <unsigned F>
 static rlscan_status launch(const ReturnsArgs& a, const Plan& plan, void* ws, hipStream_t s) {
-    ReturnsOp<F> op;
+    if (plan.geo.T < 4) {
+        ReturnsOp<F, true> op;
+        op.p = a;
+        return launch_cfg<ReturnsOp<F, true>, 4, 2>(op, plan.geo, plan.lookback, ws, 0, s);
+    }
+    ReturnsOp<F, false> op;
     op.p = a;
     return launch_g4(op, plan, ws, s);
 }

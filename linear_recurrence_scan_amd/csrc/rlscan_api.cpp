@@ -83,7 +83,12 @@ rlscan_status finish_plan(int64_t E, int64_t T, int tile, int waves, bool vec_ok
 rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
     const int64_t N = E * T;
     int tile = 0, waves = 0;
-    if (!cfg_override(tile, waves)) {
+    if (T < 4) {
+        // rows shorter than a lane's four-element group have kernels of their
+        // own, built for this one shape
+        tile = kShortRowTile;
+        waves = kShortRowWaves;
+    } else if (!cfg_override(tile, waves)) {
         // Measured on MI355X.  Tiny problems take small tiles so that more
         // workgroups share the work.  Rows of 4096 steps or longer take
         // 4096-element tiles of 8 waves x 2 segments (whole rows per tile, or

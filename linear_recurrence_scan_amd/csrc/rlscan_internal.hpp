@@ -57,6 +57,11 @@ struct Plan {
 
 rlscan_status set_error(rlscan_status st, const char* msg);
 
+// Rows shorter than the four-element lane group take one fixed launch shape
+// (2048 elements, 4 waves x 2 segments), with kernels built for it alone.
+constexpr int kShortRowTile = 2048;
+constexpr int kShortRowWaves = 4;
+
 rlscan_status launch_gae(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_vtrace(const VtraceArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s);

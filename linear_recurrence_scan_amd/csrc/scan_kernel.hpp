@@ -8,6 +8,8 @@
 //   coeffs(...) or              build (alpha, beta) in registers
 //     expectation()+finish()    (Retrace: slab staged through LDS first)
 //   epilogue<FAST>(...)         write the outputs from the scanned values
+//                               (given A, the value entering each step, alpha,
+//                               beta and Keep)
 // and the kernel runs, per tile:
 //   1. load:     every input of every segment the wave owns is requested
 //                before any arithmetic, so a wave keeps all its reads in
@@ -38,6 +40,7 @@ enum : unsigned {
     kBoot2D = 2u,        // full [E,T] bootstrap_values read alongside (with truncateds)
     kNextValues = 4u,    // TD(lambda) next_values given
     kLogpBehavior = 8u,  // V-trace log_pi_behavior given
+    kSameClip = 16u,     // V-trace rho_bar == c_bar
 };
 
 struct SegInfo {
@@ -54,6 +57,39 @@ __device__ __forceinline__ float edge_bootstrap(const float* last_value, const f
                                                 int64_t row, int64_t flat) {
     return last_value ? last_value[row] : boot[flat];
 }
+
+// Continuation value of a row end that is not read as a full [E,T] array
+// alongside the other inputs: last_value[row], or bootstrap_values[:, T-1].
+// Rows of at least G steps have at most one row end in a lane's group, so one
+// value is loaded with the group's other inputs (one register, not G).
+// Rows shorter than G (SHORT, a kernel of its own) keep one value per slot.
+template <int G, bool BACKWARD, bool SHORT>
+struct EdgeValue {
+    float v[SHORT ? G : 1];
+    __device__ void load(const Geo& g, const Tile& tl, const Grp& gr, const float* last_value,
+                         const float* boot) {
+        const uint32_t m = gr.edges & gr.valid;
+#pragma unroll
+        for (int j = 0; j < (SHORT ? G : 1); ++j) v[j] = 0.f;
+        if (!m || !(last_value || boot)) return;
+        if constexpr (SHORT) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                if (bit(m, j)) {
+                    const uint32_t o = gr.off + flat_of_slot<G, BACKWARD>(j);
+                    v[j] = edge_bootstrap(last_value, boot, row_at(g, tl, o), tl.lo + o);
+                }
+        } else {
+            const uint32_t o = gr.off + flat_of_slot<G, BACKWARD>(__builtin_ctz(m));
+            v[0] = edge_bootstrap(last_value, boot, row_at(g, tl, o), tl.lo + o);
+        }
+    }
+    // Value at slot j: 0 unless the slot is a row end inside [0, N).
+    __device__ float at(const Grp& gr, int j) const {
+        if (!bit(gr.edges & gr.valid, j)) return 0.f;
+        return v[SHORT ? j : 0];
+    }
+};
 
 template <class Op>
 struct IsStaged {
@@ -142,7 +178,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
             op.template expectation<FAST>(g, tl, seg_info(s), gr, raw[s], expect, pia);
             op.finish(gr, raw[s], expect, pia, al[s], be[s], kp[s]);
         } else {
-            op.coeffs(gr, raw[s], al[s], be[s], kp[s]);
+            op.coeffs(g, tl, gr, raw[s], al[s], be[s], kp[s]);
         }
         Affine agg{al[s][0], be[s][0]};
 #pragma unroll
@@ -203,7 +239,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
             A[j] = fmaf(be[s][j], y, al[s][j]);
             y = A[j];
         }
-        op.template epilogue<FAST>(tl, gr, A, prevA, al[s], kp[s]);
+        op.template epilogue<FAST>(tl, gr, A, prevA, al[s], be[s], kp[s]);
         xs = fmaf(segtot[s].b, xs, segtot[s].a);
     }
 }

@@ -174,6 +174,30 @@ def test_gae_without_truncations_reads_only_last_bootstrap_column():
     assert_close(adv, want, T, "advantages")
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 7, 1000, 4096])
+def test_bootstrap_column_without_truncations(T):
+    """bootstrap_values given without truncateds: only column T-1 counts, as the
+    row-end continuation value (GAE, V-trace) or carry (discounted returns);
+    rows shorter than four steps use kernels of their own."""
+    E = 300
+    rng = np.random.default_rng(T + 4)
+    r = rng.standard_normal((E, T)).astype(f32)
+    v = rng.standard_normal((E, T)).astype(f32)
+    lr = (rng.standard_normal((E, T)) * 0.5).astype(f32)
+    te = (rng.random((E, T)) < 0.05).astype(f32)
+    boot = rng.standard_normal((E, T)).astype(f32)   # interior entries must be ignored
+    adv = ops.gae(dev(r), dev(v), dev(te), None, 0.99, 0.95, dev(boot))
+    want, _ = oracle.gae(r, v, te, None, f32(0.99), f32(0.95), boot)
+    assert_close(adv, want, T, f"gae T={T}")
+    vs, pg = ops.vtrace(dev(lr), None, dev(v), dev(r), dev(te), None, 0.99, 1.0, 1.0, dev(boot))
+    want_vs, want_pg = oracle.vtrace(lr, None, v, r, te, None, f32(0.99), f32(1.0), f32(1.0), boot)
+    assert_close(vs, want_vs, T, f"vtrace vs T={T}")
+    assert_close(pg, want_pg, T, f"vtrace pg T={T}")
+    g = ops.discounted_returns(dev(r), dev(te), None, 0.99, dev(boot))
+    want_g = oracle.discounted_returns(r, te, None, f32(0.99), boot)
+    assert_close(g, want_g, T, f"discounted T={T}")
+
+
 def test_gae_unaligned_pointers():
     """Views that start 4 bytes into an allocation take the scalar-load path."""
     E, T = 33, 515
@@ -218,6 +242,14 @@ VTRACE_CASES = [
     (7, 999, True, 0.01, "trunc_last", (0.8, 1.2)),
     (40, 100, False, 0.0, None, (2.0, 0.5)),
     (2, 9000, False, 0.0, "last", (1.0, 1.0)),
+    # rows shorter than a lane's four-element group (kernels of their own)
+    (5, 2, False, 0.0, "last", (1.0, 1.0)),
+    (6, 3, True, 0.0, "last", (0.8, 1.2)),
+    (4, 1, False, 0.01, "trunc_last", (1.0, 1.0)),
+    (3, 3, True, 0.02, "2d", (1.3, 0.7)),
+    # equal and unequal clips at 8-wave tiles
+    (64, 4096, True, 0.002, "2d", (1.0, 1.0)),
+    (64, 4096, False, 0.002, "trunc_last", (1.5, 0.9)),
 ]
 
 
