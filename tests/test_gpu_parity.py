@@ -653,3 +653,74 @@ def test_lookback_results_do_not_depend_on_timing(seed):
     finally:
         ops.set_lookback_jitter(0)
     assert ops.workspace_error() == 0
+
+
+# ---------------------------------------------------------------------------
+# row lengths around every tile size the planner uses
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [255, 256, 257, 1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097])
+def test_row_lengths_around_tile_sizes(T):
+    E = max(2, 300000 // T)  # above the small-problem threshold, so the large tiles are used
+    g = synth.gae_inputs(E, T, seed=T)
+    adv = ops.gae(dev(g["rewards"]), dev(g["values"]), dev(g["terminateds"]), dev(g["truncateds"]),
+                  0.99, 0.95, dev(g["bootstrap_values"]))
+    want, _ = oracle.gae(g["rewards"], g["values"], g["terminateds"], g["truncateds"], f32(0.99),
+                         f32(0.95), g["bootstrap_values"])
+    assert_close(adv, want, T, f"gae {E}x{T}")
+    f = synth.forward_inputs(E, T, seed=T + 1)
+    got = ops.episodic_prefix_sum(dev(f["inputs"]), dev(f["dones"]), dev(f["seed_values"]))
+    want = oracle.forward_scan(f["inputs"], f["dones"], f["seed_values"], 1.0, "ends_at")
+    assert_close(got, want, T, f"prefix {E}x{T}")
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture of look-back calls
+# ---------------------------------------------------------------------------
+
+def test_lookback_calls_replay_from_a_captured_graph():
+    """The ABI enqueues only kernels (no allocation, no memset), so look-back
+    calls can be captured; the workspace epoch advances on the device, so each
+    replay sees a clean window.  Every replay is checked against the eager
+    result, with eager work on the same workspace between replays."""
+    import ctypes
+    L = ops.lib()
+    E, T = 6, 50000
+    d = synth.returns_inputs(E, T, seed=31)
+    args = [dev(d[k]) for k in ("rewards", "next_values", "terminateds", "truncateds",
+                                "bootstrap_values")]
+    out = torch.empty((E, T), device="cuda")
+    nws = int(L.rlscan_workspace_bytes(E, T))
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.Stream()
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def call():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        st = L.rlscan_returns(*[P(a) for a in args], P(out), E, T, 0.999, 0.97, P(ws), nws, s)
+        assert st == 0, L.rlscan_last_error()
+
+    with torch.cuda.stream(stream):
+        assert L.rlscan_workspace_init(P(ws), nws, ctypes.c_void_p(stream.cuda_stream)) == 0
+        call()
+    torch.cuda.synchronize()
+    eager = host(out)
+    want = oracle.lambda_returns(d["rewards"], d["next_values"], d["terminateds"], d["truncateds"],
+                                 f32(0.999), f32(0.97), d["bootstrap_values"])
+    assert_close(eager, want, T, "eager")
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        call()
+    for i in range(4):
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(out), eager, err_msg=f"replay {i}")
+        with torch.cuda.stream(stream):  # eager call on the same workspace between replays
+            call()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(out), eager, err_msg=f"eager after replay {i}")
+    err = ctypes.c_uint32(0)
+    assert L.rlscan_workspace_error(P(ws), ctypes.byref(err), ctypes.c_void_p(stream.cuda_stream)) == 0
+    assert err.value == 0
