@@ -12,6 +12,7 @@ namespace rlscan {
 struct PrefixOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = false;
+    static constexpr bool kEdgesAtLoad = true;
     static constexpr bool kFits64 = true;
     PrefixArgs p;
     struct Raw {

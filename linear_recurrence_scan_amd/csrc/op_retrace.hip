@@ -39,6 +39,7 @@ template <int KMAX>
 struct RetraceOp {
     static constexpr int G = 1;
     static constexpr bool BACKWARD = true;
+    static constexpr bool kEdgesAtLoad = false;
     static constexpr bool kFits64 = false;
     static constexpr int kSlab = KMAX > 0 ? KMAX : 1;
     RetraceArgs p;

@@ -16,6 +16,7 @@ template <unsigned F, bool SHORT>
 struct ReturnsOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = true;
+    static constexpr bool kEdgesAtLoad = (F & kTrunc) == 0;
     static constexpr bool kFits64 = true;
     ReturnsArgs p;
     struct Raw {

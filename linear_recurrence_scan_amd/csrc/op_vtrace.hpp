@@ -40,6 +40,7 @@ struct VtraceOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = true;
     static constexpr bool kSame = (F & kSameClip) != 0;
+    static constexpr bool kEdgesAtLoad = (F & kBoot2D) == 0;
     static constexpr bool kFits64 = false;
     VtraceArgs p;
     struct Raw {

@@ -158,10 +158,27 @@ __device__ __forceinline__ constexpr int flat_of_slot(int j) {
 
 __device__ __forceinline__ bool bit(uint32_t m, int j) { return (m >> j) & 1u; }
 
+// Offset and in-range mask of a group (all a load or store needs).
 template <int G, bool BACKWARD, bool FAST>
-__device__ __forceinline__ Grp make_grp(const Geo& g, const Tile& tl, uint32_t off) {
+__device__ __forceinline__ Grp make_grp_base(const Tile& tl, uint32_t off) {
     Grp r;
     r.off = off;
+    r.edges = 0;
+    if (FAST) {
+        r.valid = (1u << G) - 1u;
+    } else {
+        uint32_t valid = 0;
+#pragma unroll
+        for (int v = 0; v < G; ++v)
+            valid |= (off + (uint32_t)v < tl.rem ? 1u : 0u) << (BACKWARD ? G - 1 - v : v);
+        r.valid = valid;
+    }
+    return r;
+}
+
+// Row-end (backward) or row-start (forward) mask of the group at `off`.
+template <int G, bool BACKWARD>
+__device__ __forceinline__ uint32_t grp_edges(const Geo& g, const Tile& tl, uint32_t off) {
     const uint32_t x = tl.t_lo + off;
     uint32_t t = g.T >= (uint32_t)tl.elems ? (x >= g.T ? x - g.T : x)
                                            : x - div_small(x, g.T, g.magic) * g.T;
@@ -183,16 +200,13 @@ __device__ __forceinline__ Grp make_grp(const Geo& g, const Tile& tl, uint32_t o
             t = (t + 1u == g.T) ? 0u : t + 1u;
         }
     }
-    r.edges = edges;
-    if (FAST) {
-        r.valid = (1u << G) - 1u;
-    } else {
-        uint32_t valid = 0;
-#pragma unroll
-        for (int v = 0; v < G; ++v)
-            valid |= (off + (uint32_t)v < tl.rem ? 1u : 0u) << (BACKWARD ? G - 1 - v : v);
-        r.valid = valid;
-    }
+    return edges;
+}
+
+template <int G, bool BACKWARD, bool FAST>
+__device__ __forceinline__ Grp make_grp(const Geo& g, const Tile& tl, uint32_t off) {
+    Grp r = make_grp_base<G, BACKWARD, FAST>(tl, off);
+    r.edges = grp_edges<G, BACKWARD>(g, tl, off);
     return r;
 }
 

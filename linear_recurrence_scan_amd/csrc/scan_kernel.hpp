@@ -1,6 +1,7 @@
 // scan_kernel.hpp -- the one templated kernel every estimator runs, and its
 // launcher.  Each estimator (op_*.hip) supplies an Op with
 //   G, BACKWARD                 elements per lane and scan direction
+//   kEdgesAtLoad                load() reads row-end values (needs the mask)
 //   Raw, Keep                   raw inputs of one lane's G elements, and what
 //                               the epilogue needs besides the scan result
 //   lds_floats_per_wave()       dynamic LDS per wave (0 unless staged)
@@ -128,11 +129,13 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
         si.lds = lds_wave;
         return si;
     };
-    auto lane_grp = [&](int s) {
-        const uint32_t off = seg_off(s) + (BACKWARD ? (uint32_t)(SEG - G - lane * G)
-                                                    : (uint32_t)(lane * G));
-        return make_grp<G, BACKWARD, FAST>(g, tl, off);
+    auto lane_off = [&](int s) {
+        return seg_off(s) + (BACKWARD ? (uint32_t)(SEG - G - lane * G) : (uint32_t)(lane * G));
     };
+    // Offset and range of this lane's group in segment s; the row-end mask is
+    // added where it is needed (it costs a few dozen instructions per group).
+    auto lane_grp_base = [&](int s) { return make_grp_base<G, BACKWARD, FAST>(tl, lane_off(s)); };
+    auto lane_edges = [&](int s) { return grp_edges<G, BACKWARD>(g, tl, lane_off(s)); };
 
     // phase 1: issue every load of every segment.  When the whole grid is
     // resident at once (one round of workgroups), the waves issue their loads
@@ -142,13 +145,22 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
     // workgroups starve the epilogues of older ones, which then hold their
     // slots longer, so it stays off there.
     if (g.boost) __builtin_amdgcn_s_setprio(3);
+    // Ops that read row-end values during the load phase need the row-end
+    // mask there; for the others it is computed after every load is issued.
     Raw raw[SEGS];
     uint32_t edges[SEGS];
 #pragma unroll
     for (int s = 0; s < SEGS; ++s) {
-        const Grp gr = lane_grp(s);
-        edges[s] = gr.edges;
+        Grp gr = lane_grp_base(s);
+        if constexpr (Op::kEdgesAtLoad) gr.edges = edges[s] = lane_edges(s);
         op.template load<FAST>(g, tl, seg_info(s), gr, raw[s]);
+        // A pause of about 256 cycles between one segment's loads and the
+        // next's.  Measured on MI355X (4096 x 1024 GAE, one round of 8192
+        // waves): the loads of both segments issued back to back took 22.2 us
+        // per call, spaced by 64 cycles 22.1, by 256-512 cycles 21.0-21.2, by
+        // 1024 cycles 21.3.
+        if constexpr (FAST && G == 4)
+            if (s + 1 < SEGS) __builtin_amdgcn_s_sleep(4);
     }
 
     if (g.boost) __builtin_amdgcn_s_setprio(0);
@@ -171,8 +183,11 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
     Affine incl[SEGS], segtot[SEGS];
 #pragma unroll
     for (int s = 0; s < SEGS; ++s) {
-        Grp gr = lane_grp(s);
-        gr.edges = edges[s];
+        Grp gr = lane_grp_base(s);
+        if constexpr (Op::kEdgesAtLoad)
+            gr.edges = edges[s];
+        else
+            gr.edges = lane_edges(s);
         if constexpr (IsStaged<Op>::value) {
             float expect, pia;
             op.template expectation<FAST>(g, tl, seg_info(s), gr, raw[s], expect, pia);
@@ -228,7 +243,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
     float xs = fmaf(wexcl.b, x, wexcl.a);  // value entering this wave's first segment
 #pragma unroll
     for (int s = 0; s < SEGS; ++s) {
-        const Grp gr = lane_grp(s);
+        const Grp gr = lane_grp_base(s);  // the epilogues use the offset and range only
         const float ea = wave_shift_prev(incl[s].a, 0.f);
         const float eb = wave_shift_prev(incl[s].b, 1.f);
         float y = fmaf(eb, xs, ea);  // value entering this lane's first element
