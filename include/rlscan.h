@@ -22,6 +22,9 @@
  * - The arithmetic is fp32 (fused multiply-add allowed, any association of
  *   the scan); results agree with a float64 sequential evaluation to about
  *   1e-6 relative for T in the thousands (see the parity tests).
+ * - An empty batch (num_envs == 0 or seq_len == 0) is valid: the call checks
+ *   its scalar arguments, enqueues nothing and returns RLSCAN_OK; its array
+ *   pointers may then be NULL.
  * - Calls only enqueue work on `stream` (NULL = the default stream): no host
  *   synchronisation and no device allocation.  A call returns RLSCAN_OK once
  *   its kernel is enqueued; launch failures are reported as
@@ -81,7 +84,8 @@ const char* rlscan_status_string(rlscan_status status);
 const char* rlscan_last_error(void);
 
 /* Bytes of workspace that suffice for any entry point at this shape (the
- * Retrace entry point uses the same bound).  Returns 0 for E < 1 or T < 1. */
+ * Retrace entry point uses the same bound).  Returns 0 for an empty batch or
+ * an invalid shape. */
 size_t rlscan_workspace_bytes(int64_t num_envs, int64_t seq_len);
 
 /* Zero-fill a workspace (enqueued on `stream`, with a fill kernel so the call
@@ -120,6 +124,7 @@ rlscan_status rlscan_workspace_error(const void* ws, uint32_t* error_out, rlscan
  * Returns RLSCAN_OK when every count is zero and RLSCAN_ERR_DATA otherwise
  * (rlscan_last_error() names the failed checks).  `report` (host memory, or
  * NULL) receives the counts in both cases.
+ * An empty batch reports zero counts and returns RLSCAN_OK.
  * Errors  all four arrays NULL -> NULL_ARG; E, T out of range, or actions
  *         given with num_actions < 1 -> BAD_SHAPE; ws NULL, misaligned or too
  *         small -> WORKSPACE; a failed launch or copy -> LAUNCH.
@@ -150,8 +155,8 @@ rlscan_status rlscan_check_inputs(const float* terminateds, const float* truncat
  *         and column T-1 by contract), without truncateds only column T-1 is
  *         read.  last_value: [E] or NULL, fills column T-1 (B_{T-1}).
  * Outputs advantages [E,T]; returns [E,T] or NULL to skip.
- * Errors  NULL required pointer -> NULL_ARG; E < 1, T < 1, T >= 2^31 or
- *         E*T >= 2^46 -> BAD_SHAPE;
+ * Errors  NULL required pointer -> NULL_ARG; E < 0, T < 0, T >= 2^31 or
+ *         E*T > 2^46 -> BAD_SHAPE;
  *         last_value together with bootstrap_values or truncateds -> CONFLICT.
  */
 rlscan_status rlscan_gae(const float* rewards, const float* values, const float* terminateds,
@@ -205,7 +210,7 @@ rlscan_status rlscan_vtrace(const float* log_pi_target, const float* log_pi_beha
  *         and its outputs are then meaningless); truncateds [E,T] or NULL
  *         (no truncations).  mu_taken must be > 0.
  * Outputs q_ret [E,T]; advantages [E,T] or NULL to skip.
- * Errors  NULL_ARG; BAD_SHAPE for E, T < 1 or A outside [1, 128].
+ * Errors  NULL_ARG; BAD_SHAPE for E, T < 0 or A outside [1, 128].
  */
 rlscan_status rlscan_retrace(const float* pi_target, const float* mu_taken, const float* q_taken,
                              const float* next_q_all, const int64_t* actions,

@@ -130,13 +130,16 @@ rlscan_status plan_retrace(int64_t E, int64_t T, int64_t A, Plan& plan, bool vec
     return finish_plan(E, T, tile, waves, vec_ok, plan);
 }
 
+// E = 0 or T = 0 is valid (an empty batch: the call does nothing).
 rlscan_status check_shape(int64_t E, int64_t T) {
-    if (E < 1 || T < 1) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs and seq_len must be >= 1");
+    if (E < 0 || T < 0) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs and seq_len must be >= 0");
     if (T >= ((int64_t)1 << 31)) return set_error(RLSCAN_ERR_BAD_SHAPE, "seq_len must be < 2^31");
-    if (E > ((int64_t)1 << 40) || E > (((int64_t)1 << 46) / T))
+    if (T > 0 && (E > ((int64_t)1 << 40) || E > (((int64_t)1 << 46) / T)))
         return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
     return RLSCAN_OK;
 }
+
+bool empty_batch(int64_t E, int64_t T) { return E == 0 || T == 0; }
 
 rlscan_status check_ws(const Plan& plan, void* ws, size_t ws_bytes) {
     if (!plan.lookback) return RLSCAN_OK;
@@ -191,7 +194,7 @@ const char* rlscan_status_string(rlscan_status status) {
 const char* rlscan_last_error(void) { return g_last_error; }
 
 size_t rlscan_workspace_bytes(int64_t num_envs, int64_t seq_len) {
-    if (num_envs < 1 || seq_len < 1 || check_shape(num_envs, seq_len) != RLSCAN_OK) return 0;
+    if (check_shape(num_envs, seq_len) != RLSCAN_OK || empty_batch(num_envs, seq_len)) return 0;
     const int64_t N = num_envs * seq_len;
     return ws_bytes_for_tiles((N + kMinTile - 1) / kMinTile);
 }
@@ -222,9 +225,13 @@ rlscan_status rlscan_check_inputs(const float* terminateds, const float* truncat
                                   int64_t num_envs, int64_t seq_len, int64_t num_actions,
                                   void* ws, size_t ws_bytes, rlscan_check_report* report,
                                   rlscan_stream_t stream) {
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (empty_batch(num_envs, seq_len)) {
+        if (report) *report = rlscan_check_report{0, 0, 0, 0};
+        return RLSCAN_OK;
+    }
     if (!terminateds && !truncateds && !bootstrap_values && !actions)
         return set_error(RLSCAN_ERR_NULL_ARG, "give at least one array to check");
-    RLSCAN_TRY(check_shape(num_envs, seq_len));
     if (actions && num_actions < 1)
         return set_error(RLSCAN_ERR_BAD_SHAPE, "num_actions must be >= 1 when actions are given");
     if (!ws) return set_error(RLSCAN_ERR_WORKSPACE, "rlscan_check_inputs needs a workspace");
@@ -264,16 +271,17 @@ rlscan_status rlscan_gae(const float* rewards, const float* values, const float*
                          const float* last_value, float* advantages, float* returns,
                          int64_t num_envs, int64_t seq_len, float gamma, float lambda, void* ws,
                          size_t ws_bytes, rlscan_stream_t stream) {
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (std::isnan(gamma) || std::isnan(lambda)) return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN");
+    if (empty_batch(num_envs, seq_len)) return RLSCAN_OK;
     RLSCAN_REQUIRE(rewards, "rewards");
     RLSCAN_REQUIRE(values, "values");
     RLSCAN_REQUIRE(terminateds, "terminateds");
     RLSCAN_REQUIRE(advantages, "advantages");
-    RLSCAN_TRY(check_shape(num_envs, seq_len));
     if (last_value && bootstrap_values)
         return set_error(RLSCAN_ERR_CONFLICT, "pass either last_value or bootstrap_values, not both");
     if (last_value && truncateds)
         return set_error(RLSCAN_ERR_CONFLICT, "last_value cannot be combined with truncateds; use bootstrap_values");
-    if (std::isnan(gamma) || std::isnan(lambda)) return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN");
     const bool vec = aligned16(rewards) && aligned16(values) && aligned16(terminateds) &&
                      aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(advantages) &&
                      aligned16(returns);
@@ -291,16 +299,17 @@ rlscan_status rlscan_vtrace(const float* log_pi_target, const float* log_pi_beha
                             const float* last_value, float* vs, float* pg_advantages,
                             int64_t num_envs, int64_t seq_len, float gamma, float rho_bar,
                             float c_bar, void* ws, size_t ws_bytes, rlscan_stream_t stream) {
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (std::isnan(gamma) || std::isnan(rho_bar) || std::isnan(c_bar))
+        return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/rho_bar/c_bar is NaN");
+    if (empty_batch(num_envs, seq_len)) return RLSCAN_OK;
     RLSCAN_REQUIRE(log_pi_target, "log_pi_target");
     RLSCAN_REQUIRE(values, "values");
     RLSCAN_REQUIRE(rewards, "rewards");
     RLSCAN_REQUIRE(terminateds, "terminateds");
     RLSCAN_REQUIRE(vs, "vs");
-    RLSCAN_TRY(check_shape(num_envs, seq_len));
     if (last_value && bootstrap_values)
         return set_error(RLSCAN_ERR_CONFLICT, "pass either last_value or bootstrap_values, not both");
-    if (std::isnan(gamma) || std::isnan(rho_bar) || std::isnan(c_bar))
-        return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/rho_bar/c_bar is NaN");
     const bool vec = aligned16(log_pi_target) && aligned16(log_pi_behavior) && aligned16(values) &&
                      aligned16(rewards) && aligned16(terminateds) && aligned16(truncateds) &&
                      aligned16(bootstrap_values) && aligned16(vs) && aligned16(pg_advantages);
@@ -318,6 +327,12 @@ rlscan_status rlscan_retrace(const float* pi_target, const float* mu_taken, cons
                              float* advantages, int64_t num_envs, int64_t seq_len,
                              int64_t num_actions, float gamma, float lambda, float c_bar,
                              float rho_bar, void* ws, size_t ws_bytes, rlscan_stream_t stream) {
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (num_actions < 1 || num_actions > 128)
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_actions must lie in [1, 128]");
+    if (std::isnan(gamma) || std::isnan(lambda) || std::isnan(c_bar) || std::isnan(rho_bar))
+        return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda/c_bar/rho_bar is NaN");
+    if (empty_batch(num_envs, seq_len)) return RLSCAN_OK;
     RLSCAN_REQUIRE(pi_target, "pi_target");
     RLSCAN_REQUIRE(mu_taken, "mu_taken");
     RLSCAN_REQUIRE(q_taken, "q_taken");
@@ -326,11 +341,6 @@ rlscan_status rlscan_retrace(const float* pi_target, const float* mu_taken, cons
     RLSCAN_REQUIRE(rewards, "rewards");
     RLSCAN_REQUIRE(terminateds, "terminateds");
     RLSCAN_REQUIRE(q_ret, "q_ret");
-    RLSCAN_TRY(check_shape(num_envs, seq_len));
-    if (num_actions < 1 || num_actions > 128)
-        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_actions must lie in [1, 128]");
-    if (std::isnan(gamma) || std::isnan(lambda) || std::isnan(c_bar) || std::isnan(rho_bar))
-        return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda/c_bar/rho_bar is NaN");
     const bool vec = aligned16(pi_target) && aligned16(next_q_all);
     Plan plan;
     RLSCAN_TRY(plan_retrace(num_envs, seq_len, num_actions, plan, vec));
@@ -345,11 +355,12 @@ rlscan_status rlscan_returns(const float* rewards, const float* next_values,
                              const float* bootstrap_values, float* out, int64_t num_envs,
                              int64_t seq_len, float gamma, float lambda, void* ws, size_t ws_bytes,
                              rlscan_stream_t stream) {
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (std::isnan(gamma) || std::isnan(lambda)) return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN");
+    if (empty_batch(num_envs, seq_len)) return RLSCAN_OK;
     RLSCAN_REQUIRE(rewards, "rewards");
     RLSCAN_REQUIRE(terminateds, "terminateds");
     RLSCAN_REQUIRE(out, "out");
-    RLSCAN_TRY(check_shape(num_envs, seq_len));
-    if (std::isnan(gamma) || std::isnan(lambda)) return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN");
     const bool vec = aligned16(rewards) && aligned16(next_values) && aligned16(terminateds) &&
                      aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(out);
     Plan plan;
@@ -363,13 +374,14 @@ rlscan_status rlscan_prefix(const float* inputs, const float* dones, const float
                             int64_t num_envs, int64_t seq_len, float decay,
                             rlscan_boundary boundary, void* ws, size_t ws_bytes,
                             rlscan_stream_t stream) {
-    RLSCAN_REQUIRE(inputs, "inputs");
-    RLSCAN_REQUIRE(dones, "dones");
-    RLSCAN_REQUIRE(out, "out");
     RLSCAN_TRY(check_shape(num_envs, seq_len));
     if (boundary != RLSCAN_ENDS_AT && boundary != RLSCAN_STARTS_AT)
         return set_error(RLSCAN_ERR_BAD_PARAM, "boundary must be RLSCAN_ENDS_AT or RLSCAN_STARTS_AT");
     if (std::isnan(decay)) return set_error(RLSCAN_ERR_BAD_PARAM, "decay is NaN");
+    if (empty_batch(num_envs, seq_len)) return RLSCAN_OK;
+    RLSCAN_REQUIRE(inputs, "inputs");
+    RLSCAN_REQUIRE(dones, "dones");
+    RLSCAN_REQUIRE(out, "out");
     const bool vec = aligned16(inputs) && aligned16(dones) && aligned16(out);
     Plan plan;
     RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));

@@ -72,9 +72,11 @@ def test_gae_validation(L):
     assert gae(L, v=N) == NULL_ARG
     assert gae(L, te=N) == NULL_ARG
     assert gae(L, adv=N) == NULL_ARG
-    assert gae(L, E=0) == BAD_SHAPE
-    assert gae(L, T=0) == BAD_SHAPE
+    assert gae(L, E=0) == OK and gae(L, T=0) == OK          # empty batch: nothing to do
+    assert gae(L, r=N, v=N, te=N, adv=N, E=0) == OK         # (empty tensors may have NULL data)
     assert gae(L, E=-3) == BAD_SHAPE
+    assert gae(L, T=-1) == BAD_SHAPE
+    assert gae(L, T=1 << 31) == BAD_SHAPE
     assert gae(L, E=1 << 45, T=1 << 20) == BAD_SHAPE
     assert gae(L, lv=P, bv=P) == CONFLICT
     assert gae(L, lv=P, tr=P) == CONFLICT
@@ -103,7 +105,8 @@ def test_vtrace_validation(L):
     assert call(r=N) == NULL_ARG
     assert call(te=N) == NULL_ARG
     assert call(vs=N) == NULL_ARG
-    assert call(T=0) == BAD_SHAPE
+    assert call(T=0) == OK
+    assert call(T=-2) == BAD_SHAPE
     assert call(lv=P, bv=P) == CONFLICT
     assert call(rb=float("nan")) == BAD_PARAM
 
@@ -116,14 +119,16 @@ def test_retrace_validation(L):
         assert call(**{kw: N}) == NULL_ARG, kw
     assert call(A=0) == BAD_SHAPE
     assert call(A=129) == BAD_SHAPE
-    assert call(E=0) == BAD_SHAPE
+    assert call(E=0) == OK
+    assert call(E=0, A=0) == BAD_SHAPE
 
 
 def test_returns_and_prefix_validation(L):
     assert L.rlscan_returns(N, N, P, N, N, P, 4, 8, 0.99, 0.9, N, 0, N) == NULL_ARG
     assert L.rlscan_returns(P, N, N, N, N, P, 4, 8, 0.99, 0.9, N, 0, N) == NULL_ARG
     assert L.rlscan_returns(P, N, P, N, N, N, 4, 8, 0.99, 0.9, N, 0, N) == NULL_ARG
-    assert L.rlscan_returns(P, N, P, N, N, P, 4, 0, 0.99, 0.9, N, 0, N) == BAD_SHAPE
+    assert L.rlscan_returns(P, N, P, N, N, P, 4, 0, 0.99, 0.9, N, 0, N) == OK
+    assert L.rlscan_returns(P, N, P, N, N, P, -4, 8, 0.99, 0.9, N, 0, N) == BAD_SHAPE
     assert L.rlscan_prefix(N, P, N, P, 4, 8, 1.0, 0, N, 0, N) == NULL_ARG
     assert L.rlscan_prefix(P, N, N, P, 4, 8, 1.0, 0, N, 0, N) == NULL_ARG
     assert L.rlscan_prefix(P, P, N, N, 4, 8, 1.0, 0, N, 0, N) == NULL_ARG
@@ -135,8 +140,8 @@ def test_check_inputs_validation(L):
     def call(te=P, tr=N, bv=N, act=N, E=4, T=8, A=0, ws=ctypes.c_void_p(0x100000), nws=1 << 16):
         return L.rlscan_check_inputs(te, tr, bv, act, E, T, A, ws, nws, N, N)
     assert call(te=N) == NULL_ARG
-    assert call(E=0) == BAD_SHAPE
-    assert call(T=0) == BAD_SHAPE
+    assert call(E=0) == OK
+    assert call(T=-1) == BAD_SHAPE
     assert call(act=P, A=0) == BAD_SHAPE
     assert call(ws=N) == WORKSPACE
     assert call(ws=ctypes.c_void_p(0x100040)) == WORKSPACE

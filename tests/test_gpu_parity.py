@@ -724,3 +724,76 @@ def test_lookback_calls_replay_from_a_captured_graph():
     err = ctypes.c_uint32(0)
     assert L.rlscan_workspace_error(P(ws), ctypes.byref(err), ctypes.c_void_p(stream.cuda_stream)) == 0
     assert err.value == 0
+
+
+# ---------------------------------------------------------------------------
+# empty batches and the largest shapes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(0, 16), (5, 0), (0, 0)])
+def test_empty_batches_are_no_ops(shape):
+    E, T = shape
+    z = torch.zeros(shape, device="cuda")
+    adv, ret = ops.gae(z, z, z, z, 0.99, 0.95, z, want_returns=True)
+    assert adv.shape == shape and ret.shape == shape
+    vs, pg = ops.vtrace(z, None, z, z, z, None, 0.99, 1.0, 1.0, None, torch.zeros(E, device="cuda"))
+    assert vs.shape == shape
+    assert ops.discounted_returns(z, z, z, 0.99, z).shape == shape
+    assert ops.episodic_prefix_sum(z, z).shape == shape
+    pi = torch.zeros((E, T, 3), device="cuda")
+    q, a = ops.retrace(pi, z, z, pi, torch.zeros(shape, dtype=torch.int64, device="cuda"), z, z)
+    assert q.shape == shape
+    assert ops.check_inputs(z, z, z)["ok"]
+
+
+def _device_rollout(E, T, seed, p_term):
+    """Seeded rollout generated on the device (torch's generator), so that
+    shapes too large for host-side generation can be tested."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    r = torch.randn((E, T), device="cuda", generator=gen)
+    v = torch.randn((E, T), device="cuda", generator=gen)
+    te = (torch.rand((E, T), device="cuda", generator=gen) < p_term).float()
+    return r, v, te
+
+
+def test_more_than_2_pow_32_elements():
+    """4100 x 1048576 = 4.3e9 steps (flat indices beyond 32 bits): rows near
+    the end of the buffer are checked whole against the oracle."""
+    E, T = 4100, 1 << 20
+    r, v, te = _device_rollout(E, T, seed=123, p_term=1e-3)
+    last = torch.randn(E, device="cuda")
+    adv = ops.gae(r, v, te, None, 0.99, 0.95, last_value=last)
+    for row in (0, 2047, E - 2, E - 1):
+        pick = lambda t: t[row:row + 1].cpu().numpy()
+        want, _ = oracle.gae(pick(r), pick(v), pick(te), None, f32(0.99), f32(0.95),
+                             last_value=last[row:row + 1].cpu().numpy())
+        assert_close(adv[row:row + 1], want, 4096, f"row {row}")
+    del r, v, te, adv
+    torch.cuda.empty_cache()
+
+
+def test_longest_rows():
+    """Rows of 2^31 - 1 steps (the largest seq_len): windows that end at a
+    terminated step depend on nothing after it, so the oracle checks such
+    windows at the start, middle and end of each row; the long rows cross
+    half a million tiles each through the look-back."""
+    E, T = 2, (1 << 31) - 1
+    r, _, te = _device_rollout(E, T, seed=7, p_term=1e-4)
+    del _
+    torch.cuda.empty_cache()
+    g = ops.discounted_returns(r, te, None, 0.999)
+    for row in range(E):
+        ends = torch.nonzero(te[row]).flatten()
+        for k in (0, len(ends) // 2, len(ends) - 1):
+            b = int(ends[k]) + 1
+            a = max(0, b - 50000)
+            sl = lambda t: t[row:row + 1, a:b].cpu().numpy()
+            want = oracle.discounted_returns(sl(r), sl(te), None, f32(0.999))
+            assert_close(g[row:row + 1, a:b], want, 131072, f"row {row} window [{a}, {b})")
+        # the row's last steps depend only on the steps after them
+        sl = lambda t: t[row:row + 1, T - 50000:].cpu().numpy()
+        want = oracle.discounted_returns(sl(r), sl(te), None, f32(0.999))
+        assert_close(g[row:row + 1, T - 50000:], want, 131072, f"row {row} tail")
+    del r, te, g
+    torch.cuda.empty_cache()
