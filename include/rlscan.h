@@ -166,6 +166,25 @@ rlscan_status rlscan_gae(const float* rewards, const float* values, const float*
                          void* ws, size_t ws_bytes, rlscan_stream_t stream);
 
 /*
+ * GAE over the compact rollout format -- the recurrence of rlscan_gae (same
+ * sources), with bf16 storage: rewards, values, bootstrap_values,
+ * last_value, advantages and returns are bfloat16 (raw 16-bit patterns in
+ * uint16_t arrays), terminateds and truncateds are one byte each holding 0
+ * or 1.  That is 12 bytes per step with both outputs, against 28 for
+ * rlscan_gae.  The paper lists bf16 input/output among its planned systems
+ * work (Sec. 9.3) and warns that a bf16 accumulation drifts over long rows
+ * (Sec. 4.4): the arithmetic here is fp32, the inputs widen to fp32 exactly,
+ * and each output is rounded to bf16 (nearest, ties to even) when stored.
+ * Arguments, NULL rules, conflicts and errors are those of rlscan_gae.
+ */
+rlscan_status rlscan_gae_bf16(const uint16_t* rewards, const uint16_t* values,
+                              const uint8_t* terminateds, const uint8_t* truncateds,
+                              const uint16_t* bootstrap_values, const uint16_t* last_value,
+                              uint16_t* advantages, uint16_t* returns, int64_t num_envs,
+                              int64_t seq_len, float gamma, float lambda, void* ws,
+                              size_t ws_bytes, rlscan_stream_t stream);
+
+/*
  * V-trace -- kernels page, API Reference: compute_vtrace (Recurrence,
  * Outputs); paper Sec. 3.3.2 and Table 1.
  *   rho_hat_t = exp(log_pi_target_t - log_pi_behavior_t)

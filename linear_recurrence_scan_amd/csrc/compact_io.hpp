@@ -1,0 +1,71 @@
+// compact_io.hpp -- loads and stores of the compact rollout formats: bf16
+// values (rewards, values, bootstrap values, outputs) and one-byte 0/1 flags.
+// Arithmetic stays fp32: bf16 widens to fp32 exactly, and results are rounded
+// to bf16 (nearest, ties to even) only when stored.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "scan_core.hpp"
+
+namespace rlscan {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+// A lane's four consecutive bf16 values (8 bytes), widened, in scan order.
+// FAST: one 8-byte load (the tile is whole and the array 8-byte aligned).
+template <bool BACKWARD, bool FAST>
+__device__ __forceinline__ void load_bf16_group(const __bf16* __restrict__ tp, const Grp& gr,
+                                                float (&out)[4]) {
+    if constexpr (FAST) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tp + gr.off));
+        const float f[4] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[BACKWARD ? 3 - k : k] = f[k];
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            out[j] = bit(gr.valid, j) ? (float)tp[gr.off + flat_of_slot<4, BACKWARD>(j)] : 0.f;
+    }
+}
+
+// A lane's four consecutive one-byte flags (4 bytes) as 0.0f / 1.0f.
+template <bool BACKWARD, bool FAST>
+__device__ __forceinline__ void load_u8_group(const uint8_t* __restrict__ tp, const Grp& gr,
+                                              float (&out)[4]) {
+    if constexpr (FAST) {
+        const uint32_t v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tp + gr.off));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) out[BACKWARD ? 3 - k : k] = (float)((v >> (8 * k)) & 0xffu);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            out[j] = bit(gr.valid, j) ? (float)tp[gr.off + flat_of_slot<4, BACKWARD>(j)] : 0.f;
+    }
+}
+
+template <bool BACKWARD, bool FAST>
+__device__ __forceinline__ void store_bf16_group(__bf16* __restrict__ tp, const Grp& gr,
+                                                 const float (&in)[4]) {
+    if constexpr (FAST) {
+        u32x2 v;
+        v.x = pack_bf16(in[BACKWARD ? 3 : 0], in[BACKWARD ? 2 : 1]);
+        v.y = pack_bf16(in[BACKWARD ? 1 : 2], in[BACKWARD ? 0 : 3]);
+        *reinterpret_cast<u32x2*>(tp + gr.off) = v;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (bit(gr.valid, j)) tp[gr.off + flat_of_slot<4, BACKWARD>(j)] = (__bf16)in[j];
+    }
+}
+
+}  // namespace rlscan

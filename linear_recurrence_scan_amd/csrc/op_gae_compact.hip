@@ -1,0 +1,103 @@
+// op_gae_compact.hip -- GAE over the compact rollout format: bf16 rewards,
+// values, bootstrap values and outputs, one-byte terminated/truncated flags
+// (12 bytes per step with both outputs instead of 28).  The recurrence is the
+// one of op_gae.hip (rl-triton kernels page, compute_gae; paper Sec. 3.3.1,
+// Table 1), evaluated in fp32.  The paper lists bf16 input/output among its
+// planned systems work (Sec. 9.3) and explains why the accumulation itself
+// must not be bf16 (Sec. 4.4: a bf16 scan drifts over long rows), so only the
+// storage is bf16 here.
+#include "compact_io.hpp"
+#include "scan_kernel.hpp"
+
+namespace rlscan {
+
+template <unsigned F, bool SHORT>
+struct GaeCompactOp {
+    static constexpr int G = 4;
+    static constexpr bool BACKWARD = true;
+    static constexpr bool kEdgesAtLoad = (F & kTrunc) == 0;
+    static constexpr bool kFits64 = true;
+    GaeCompactArgs p;
+    struct Raw {
+        float R[G], V[G], TE[G], TR[G], B[G];
+        float halo;
+        EdgeValue<G, true, SHORT> eb;
+    };
+    struct Keep {
+        float v;
+    };
+    __device__ size_t lds_floats_per_wave() const { return 0; }
+
+    __device__ const __bf16* bf(const uint16_t* q) const { return reinterpret_cast<const __bf16*>(q); }
+
+    template <bool FAST>
+    __device__ void load(const Geo& g, const Tile& tl, const SegInfo& si, const Grp& gr,
+                         Raw& w) const {
+        load_bf16_group<true, FAST>(bf(p.rewards) + tl.lo, gr, w.R);
+        load_bf16_group<true, FAST>(bf(p.values) + tl.lo, gr, w.V);
+        load_u8_group<true, FAST>(p.terminateds + tl.lo, gr, w.TE);
+#pragma unroll
+        for (int j = 0; j < G; ++j) w.TR[j] = w.B[j] = 0.f;
+        if constexpr ((F & kTrunc) != 0) {
+            load_u8_group<true, FAST>(p.truncateds + tl.lo, gr, w.TR);
+            if constexpr ((F & kBoot2D) != 0)
+                load_bf16_group<true, FAST>(bf(p.bootstrap_values) + tl.lo, gr, w.B);
+        } else {
+            w.eb.load(g, tl, gr, bf(p.last_value), bf(p.bootstrap_values));
+        }
+        w.halo = (lane_id() == 0 && si.halo_valid) ? (float)bf(p.values)[si.halo_flat] : 0.f;
+    }
+
+    __device__ void coeffs(const Geo& g, const Tile& tl, const Grp& gr, const Raw& w,
+                           float (&al)[G], float (&be)[G], Keep (&kp)[G]) const {
+        float VN[G];
+        scan_prev<G>(w.V, w.halo, VN);
+        const float gl = p.gamma * p.lambda;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const bool edge = bit(gr.edges, j);
+            float b = w.B[j];
+            if constexpr ((F & kTrunc) == 0) b = w.eb.at(gr, j);
+            const float vnext = edge ? b : fmaf(1.f - w.TR[j], VN[j], b);
+            const float done = fminf(w.TE[j] + w.TR[j], 1.f);
+            const float a = fmaf(p.gamma * (1.f - w.TE[j]), vnext, w.R[j]) - w.V[j];
+            const float bb = edge ? 0.f : gl * (1.f - done);  // A_T = 0
+            al[j] = bit(gr.valid, j) ? a : 0.f;
+            be[j] = bit(gr.valid, j) ? bb : 1.f;
+            kp[j].v = w.V[j];
+        }
+    }
+
+    template <bool FAST>
+    __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
+                             const float (&)[G], const float (&)[G], const Keep (&kp)[G]) const {
+        store_bf16_group<true, FAST>(reinterpret_cast<__bf16*>(p.advantages) + tl.lo, gr, A);
+        if (p.returns) {
+            float R[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) R[j] = A[j] + kp[j].v;
+            store_bf16_group<true, FAST>(reinterpret_cast<__bf16*>(p.returns) + tl.lo, gr, R);
+        }
+    }
+};
+
+template <unsigned F>
+static rlscan_status launch(const GaeCompactArgs& a, const Plan& plan, void* ws, hipStream_t s) {
+    if (plan.geo.T < 4) {
+        GaeCompactOp<F, true> op;
+        op.p = a;
+        return launch_cfg<GaeCompactOp<F, true>, 4, 2>(op, plan.geo, plan.lookback, ws, 0, s);
+    }
+    GaeCompactOp<F, false> op;
+    op.p = a;
+    return launch_g4(op, plan, ws, s);
+}
+
+rlscan_status launch_gae_compact(const GaeCompactArgs& a, const Plan& plan, void* ws,
+                                 hipStream_t s) {
+    if (!a.truncateds) return launch<0>(a, plan, ws, s);
+    if (!a.bootstrap_values) return launch<kTrunc>(a, plan, ws, s);
+    return launch<kTrunc | kBoot2D>(a, plan, ws, s);
+}
+
+}  // namespace rlscan

@@ -37,7 +37,7 @@ struct ReturnsOp {
             if constexpr ((F & kBoot2D) != 0)
                 load_group<G, true, FAST>(p.bootstrap_values + tl.lo, gr, w.B);
         } else {
-            w.eb.load(g, tl, gr, nullptr, p.bootstrap_values);
+            w.eb.load(g, tl, gr, static_cast<const float*>(nullptr), p.bootstrap_values);
         }
         if constexpr ((F & kNextValues) != 0)
             load_group<G, true, FAST>(p.next_values + tl.lo, gr, w.NV);

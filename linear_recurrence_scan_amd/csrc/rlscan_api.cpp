@@ -293,6 +293,36 @@ rlscan_status rlscan_gae(const float* rewards, const float* values, const float*
     return launch_gae(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
+rlscan_status rlscan_gae_bf16(const uint16_t* rewards, const uint16_t* values,
+                              const uint8_t* terminateds, const uint8_t* truncateds,
+                              const uint16_t* bootstrap_values, const uint16_t* last_value,
+                              uint16_t* advantages, uint16_t* returns, int64_t num_envs,
+                              int64_t seq_len, float gamma, float lambda, void* ws,
+                              size_t ws_bytes, rlscan_stream_t stream) {
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (std::isnan(gamma) || std::isnan(lambda)) return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN");
+    if (empty_batch(num_envs, seq_len)) return RLSCAN_OK;
+    RLSCAN_REQUIRE(rewards, "rewards");
+    RLSCAN_REQUIRE(values, "values");
+    RLSCAN_REQUIRE(terminateds, "terminateds");
+    RLSCAN_REQUIRE(advantages, "advantages");
+    if (last_value && bootstrap_values)
+        return set_error(RLSCAN_ERR_CONFLICT, "pass either last_value or bootstrap_values, not both");
+    if (last_value && truncateds)
+        return set_error(RLSCAN_ERR_CONFLICT, "last_value cannot be combined with truncateds; use bootstrap_values");
+    // 8-byte groups of four bf16 values and 4-byte groups of four flags
+    auto a8 = [](const void* q) { return q == nullptr || (reinterpret_cast<uintptr_t>(q) & 7u) == 0; };
+    auto a4 = [](const void* q) { return q == nullptr || (reinterpret_cast<uintptr_t>(q) & 3u) == 0; };
+    const bool vec = a8(rewards) && a8(values) && a4(terminateds) && a4(truncateds) &&
+                     a8(bootstrap_values) && a8(advantages) && a8(returns);
+    Plan plan;
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
+    GaeCompactArgs a{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+                     advantages, returns, gamma, lambda};
+    return launch_gae_compact(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
 rlscan_status rlscan_vtrace(const float* log_pi_target, const float* log_pi_behavior,
                             const float* values, const float* rewards, const float* terminateds,
                             const float* truncateds, const float* bootstrap_values,

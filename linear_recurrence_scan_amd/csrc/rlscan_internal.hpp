@@ -18,6 +18,15 @@ struct GaeArgs {
     float gamma, lambda;
 };
 
+// Compact rollout format: bf16 values (raw 16-bit storage), one-byte flags.
+struct GaeCompactArgs {
+    const uint16_t *rewards, *values;
+    const uint8_t *terminateds, *truncateds;
+    const uint16_t *bootstrap_values, *last_value;
+    uint16_t *advantages, *returns;
+    float gamma, lambda;
+};
+
 struct VtraceArgs {
     const float *log_pi_target, *log_pi_behavior, *values, *rewards, *terminateds, *truncateds,
         *bootstrap_values, *last_value;
@@ -63,6 +72,7 @@ constexpr int kShortRowTile = 2048;
 constexpr int kShortRowWaves = 4;
 
 rlscan_status launch_gae(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
+rlscan_status launch_gae_compact(const GaeCompactArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_vtrace(const VtraceArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s);
 // 16-byte pieces of each 3-D array a lane holds per segment for A actions (0:

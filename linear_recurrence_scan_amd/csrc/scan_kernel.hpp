@@ -54,9 +54,10 @@ struct SegInfo {
 // Continuation value at a row end when it does not come from a full [E,T]
 // bootstrap array read alongside the other inputs: last_value[row], or
 // column T-1 of bootstrap_values when there are no truncations.
-__device__ __forceinline__ float edge_bootstrap(const float* last_value, const float* boot,
-                                                int64_t row, int64_t flat) {
-    return last_value ? last_value[row] : boot[flat];
+template <class P>
+__device__ __forceinline__ float edge_bootstrap(const P* last_value, const P* boot, int64_t row,
+                                                int64_t flat) {
+    return last_value ? (float)last_value[row] : (float)boot[flat];
 }
 
 // Continuation value of a row end that is not read as a full [E,T] array
@@ -67,8 +68,9 @@ __device__ __forceinline__ float edge_bootstrap(const float* last_value, const f
 template <int G, bool BACKWARD, bool SHORT>
 struct EdgeValue {
     float v[SHORT ? G : 1];
-    __device__ void load(const Geo& g, const Tile& tl, const Grp& gr, const float* last_value,
-                         const float* boot) {
+    template <class P>
+    __device__ void load(const Geo& g, const Tile& tl, const Grp& gr, const P* last_value,
+                         const P* boot) {
         const uint32_t m = gr.edges & gr.valid;
 #pragma unroll
         for (int j = 0; j < (SHORT ? G : 1); ++j) v[j] = 0.f;

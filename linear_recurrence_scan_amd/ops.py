@@ -75,6 +75,7 @@ def _declare(L):
     L.rlscan_workspace_init.argtypes = [vp, sz, vp]
     L.rlscan_workspace_error.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     L.rlscan_gae.argtypes = [vp] * 8 + [i64, i64, f32, f32, vp, sz, vp]
+    L.rlscan_gae_bf16.argtypes = [vp] * 8 + [i64, i64, f32, f32, vp, sz, vp]
     L.rlscan_vtrace.argtypes = [vp] * 10 + [i64, i64, f32, f32, f32, vp, sz, vp]
     L.rlscan_retrace.argtypes = [vp] * 10 + [i64, i64, i64, f32, f32, f32, f32, vp, sz, vp]
     L.rlscan_returns.argtypes = [vp] * 6 + [i64, i64, f32, f32, vp, sz, vp]
@@ -85,7 +86,7 @@ def _declare(L):
     L.rlscan_check_inputs.argtypes = [vp] * 4 + [i64, i64, i64, vp, sz,
                                                  ctypes.POINTER(CheckReport), vp]
     for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
-                 "rlscan_gae", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
+                 "rlscan_gae", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
                  "rlscan_check_inputs", "rlscan_debug_set_launch_shape",
                  "rlscan_debug_set_lookback_jitter"):
         getattr(L, name).restype = st
@@ -106,15 +107,16 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _f32(name, t, shape=None, device=None, optional=False):
+def _typed(name, t, dtypes, shape=None, device=None, optional=False):
     if t is None:
         if optional:
             return None
         raise ValueError(f"{name} is required")
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.dtype != torch.float32:
-        raise TypeError(f"{name}: expected float32, got {t.dtype}")
+    if t.dtype not in dtypes:
+        want = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise TypeError(f"{name}: expected {want}, got {t.dtype}")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must be on a GPU (got {t.device})")
     if device is not None and t.device != device:
@@ -122,6 +124,19 @@ def _f32(name, t, shape=None, device=None, optional=False):
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} shape {tuple(t.shape)} != {tuple(shape)}")
     return t.contiguous()
+
+
+def _f32(name, t, shape=None, device=None, optional=False):
+    return _typed(name, t, (torch.float32,), shape, device, optional)
+
+
+def _bf16(name, t, shape=None, device=None, optional=False):
+    return _typed(name, t, (torch.bfloat16,), shape, device, optional)
+
+
+def _flag8(name, t, shape=None, device=None, optional=False):
+    """One-byte 0/1 flags: uint8 or bool (both store 0 and 1 as one byte)."""
+    return _typed(name, t, (torch.uint8, torch.bool), shape, device, optional)
 
 
 def _shape2(name, t):
@@ -220,6 +235,18 @@ def rlscan_gae(rewards, values, terminateds, truncateds, bootstrap_values, last_
     _check("rlscan_gae", st)
 
 
+def rlscan_gae_bf16(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+                    advantages, returns, gamma, lambda_):
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    ws, nws = workspace(dev, E, T)
+    st = lib().rlscan_gae_bf16(_ptr(rewards), _ptr(values), _ptr(terminateds), _ptr(truncateds),
+                               _ptr(bootstrap_values), _ptr(last_value), _ptr(advantages),
+                               _ptr(returns), E, T, float(gamma), float(lambda_), _ptr(ws), nws,
+                               _stream(dev))
+    _check("rlscan_gae_bf16", st)
+
+
 def rlscan_vtrace(log_pi_target, log_pi_behavior, values, rewards, terminateds, truncateds,
                   bootstrap_values, last_value, vs, pg_advantages, gamma, rho_bar, c_bar):
     E, T = _shape2("rewards", rewards)
@@ -306,6 +333,28 @@ def gae(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
     adv = torch.empty_like(r)
     ret = torch.empty_like(r) if want_returns else None
     rlscan_gae(r, v, te, tr, bv, lv, adv, ret, gamma, lambda_)
+    return (adv, ret) if want_returns else adv
+
+
+def gae_bf16(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
+             bootstrap_values=None, last_value=None, want_returns=False):
+    """GAE over the compact format: bfloat16 rewards/values/bootstrap values
+    and outputs, uint8 (or bool) 0/1 flags; fp32 arithmetic on chip."""
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    r = _bf16("rewards", rewards, (E, T))
+    v = _bf16("values", values, (E, T), dev)
+    te = _flag8("terminateds", terminateds, (E, T), dev)
+    tr = _flag8("truncateds", truncateds, (E, T), dev, optional=True)
+    bv = _bf16("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
+    lv = _bf16("last_value", last_value, (E,), dev, optional=True)
+    if _checks_enabled():
+        _debug_check("gae_bf16", terminateds=te.float(),
+                     truncateds=None if tr is None else tr.float(),
+                     bootstrap_values=None if bv is None else bv.float())
+    adv = torch.empty_like(r)
+    ret = torch.empty_like(r) if want_returns else None
+    rlscan_gae_bf16(r, v, te, tr, bv, lv, adv, ret, gamma, lambda_)
     return (adv, ret) if want_returns else adv
 
 

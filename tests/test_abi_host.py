@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
-    for n in ("rlscan_gae", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
+    for n in ("rlscan_gae", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
         assert n in names
 
 
@@ -81,6 +81,22 @@ def test_gae_validation(L):
     assert gae(L, lv=P, bv=P) == CONFLICT
     assert gae(L, lv=P, tr=P) == CONFLICT
     assert L.rlscan_gae(P, P, P, N, N, N, P, N, 4, 8, float("nan"), 0.95, N, 0, N) == BAD_PARAM
+
+
+def test_gae_bf16_validation(L):
+    def call(r=P, v=P, te=P, tr=N, bv=N, lv=N, adv=P, ret=N, E=4, T=8, g=0.99, ws=N, nws=0):
+        return L.rlscan_gae_bf16(r, v, te, tr, bv, lv, adv, ret, E, T, g, 0.95, ws, nws, N)
+    for kw in ("r", "v", "te", "adv"):
+        assert call(**{kw: N}) == NULL_ARG, kw
+    assert call(r=N, v=N, te=N, adv=N, E=0) == OK
+    assert call(T=0) == OK
+    assert call(E=-1) == BAD_SHAPE
+    assert call(lv=P, bv=P) == CONFLICT
+    assert call(lv=P, tr=P) == CONFLICT
+    assert call(g=float("nan")) == BAD_PARAM
+    assert call(E=4096, T=1000) == WORKSPACE
+    # a NULL/0 workspace is enough when no row straddles a tile
+    assert L.rlscan_workspace_bytes(4096, 1024) >= 256
 
 
 def test_lookback_shapes_require_workspace(L):
