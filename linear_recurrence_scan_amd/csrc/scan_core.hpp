@@ -28,14 +28,8 @@ namespace rlscan {
 
 constexpr int kWave = 64;
 
-// DPP controls of the gfx9 encoding.
-constexpr int kRowShr1 = 0x111;
-constexpr int kRowShr2 = 0x112;
-constexpr int kRowShr4 = 0x114;
-constexpr int kRowShr8 = 0x118;
+// DPP control of the gfx9 encoding: every lane reads lane l-1.
 constexpr int kWaveShr1 = 0x138;
-constexpr int kRowBcast15 = 0x142;
-constexpr int kRowBcast31 = 0x143;
 
 struct Affine {
     float a, b;  // x -> a + b*x
@@ -65,27 +59,47 @@ __device__ __forceinline__ uint64_t readfirstlane_u64(uint64_t x) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// One Hillis-Steele step.  A lane whose source lane does not exist (shifted
-// in from outside its 16-lane row, or a row the row mask leaves out) keeps
-// DPP's "old" operand, which is the identity map, so the combine is a no-op
-// there without any select.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ Affine scan_step(Affine x) {
-    const float sa = dpp<CTRL, ROW_MASK>(0.f, x.a);
-    const float sb = dpp<CTRL, ROW_MASK>(1.f, x.b);
-    return Affine{fmaf(x.b, sa, x.a), x.b * sb};
-}
-
 // Inclusive scan over the 64 lanes of a wave: lane l receives
-// x_l o x_{l-1} o ... o x_0.  Must be called by all 64 lanes.
+// x_l o x_{l-1} o ... o x_0.  Must be called by all 64 lanes (full EXEC).
+//
+// Six Hillis-Steele steps (row_shr 1/2/4/8 inside each 16-lane row, then
+// row_bcast 15 and 31 across rows), each one pair of DPP instructions that
+// read the shifted operand straight from the other lane:
+//   v_fmac_f32_dpp a, a, b   a_l <- a_{l-k} * b_l + a_l   (one rounding, as fmaf)
+//   v_mul_f32_dpp  b, b, b   b_l <- b_{l-k} * b_l
+// The fmac runs first, so it sees the lane's own b before the step.  DPP
+// with bound control off does not write a lane whose source lane is out of
+// range or whose row the row mask leaves out, so those lanes keep their map,
+// which is what composing with the identity would give.  A VALU write of a
+// VGPR that a DPP instruction then reads needs two wait states: the s_nop 1
+// between steps covers both operands (and s_nop 4 at entry the five states a
+// preceding EXEC write needs).  Written as inline assembly because the
+// compiler keeps the identity as a separate "old" register and spends three
+// extra moves per step on it.
 __device__ __forceinline__ Affine wave_inclusive_scan(Affine x) {
-    x = scan_step<kRowShr1, 0xf>(x);
-    x = scan_step<kRowShr2, 0xf>(x);
-    x = scan_step<kRowShr4, 0xf>(x);
-    x = scan_step<kRowShr8, 0xf>(x);
-    x = scan_step<kRowBcast15, 0xa>(x);
-    x = scan_step<kRowBcast31, 0xc>(x);
-    return x;
+    float a = x.a, b = x.b;
+    asm volatile(
+        "s_nop 4\n\t"
+        "v_fmac_f32_dpp %0, %0, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %1 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_fmac_f32_dpp %0, %0, %1 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+        "v_mul_f32_dpp %1, %1, %1 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+v"(a), "+v"(b));
+    return Affine{a, b};
 }
 
 // Value of lane l-1 for every lane l; lane 0 receives `lane0`.
