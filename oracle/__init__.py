@@ -48,13 +48,14 @@ def configure(lib):
     """Declare the C signatures on a loaded oracle library."""
     i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
     lib.ora_gae.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, dbl, dbl, vp, vp]
+    lib.ora_gae_skip.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, vp, dbl, dbl, vp, vp]
     lib.ora_vtrace.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, vp, vp, dbl, dbl, dbl, vp, vp]
     lib.ora_retrace.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp,
                                 dbl, dbl, dbl, dbl, vp, vp]
     lib.ora_lambda_returns.argtypes = [i64, i64, vp, vp, vp, vp, vp, dbl, dbl, vp]
     lib.ora_discounted_returns.argtypes = [i64, i64, vp, vp, vp, vp, dbl, vp]
     lib.ora_forward_scan.argtypes = [i64, i64, vp, vp, vp, dbl, ctypes.c_int, vp]
-    for name in ("ora_gae", "ora_vtrace", "ora_retrace", "ora_lambda_returns",
+    for name in ("ora_gae", "ora_gae_skip", "ora_vtrace", "ora_retrace", "ora_lambda_returns",
                  "ora_discounted_returns", "ora_forward_scan"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -105,6 +106,22 @@ def gae(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
     rc = _load().ora_gae(E, T, _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(lv),
                          float(gamma), float(lambda_), _ptr(adv), _ptr(ret))
     _check(rc, "gae")
+    return adv, ret
+
+
+def gae_skip(rewards, values, terminateds, skip_mask, truncateds=None, gamma=0.99, lambda_=0.95,
+             bootstrap_values=None, last_value=None):
+    """GAE with an observation-skip mask (1 = masked token), float64."""
+    E, T = _shape(rewards)
+    r, v, te = _f32(rewards, (E, T)), _f32(values, (E, T)), _f32(terminateds, (E, T))
+    sk = _f32(skip_mask, (E, T))
+    tr, bv = _f32(truncateds, (E, T)), _f32(bootstrap_values, (E, T))
+    lv = _f32(last_value, (E,))
+    adv = np.empty((E, T), np.float64)
+    ret = np.empty((E, T), np.float64)
+    rc = _load().ora_gae_skip(E, T, _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(lv),
+                              _ptr(sk), float(gamma), float(lambda_), _ptr(adv), _ptr(ret))
+    _check(rc, "gae_skip")
     return adv, ret
 
 

@@ -102,6 +102,49 @@ int ora_gae(int64_t E, int64_t T, const float* rewards, const float* values,
 }
 
 /*
+ * GAE with an observation-skip mask ([P] Sec. 9.3: for multi-turn and
+ * tool-use rows the recurrence is carried across masked tokens, beta_t = 1).
+ * Reading, where the paper gives only beta_t = 1:
+ *   unmasked t (skip_t = 0): exactly the GAE step above;
+ *   masked t   (skip_t = 1): A_t = (1 - done_t) A_{t+1}, A_T = 0
+ *     (alpha_t = 0: the token adds no TD error; an episode end flagged on a
+ *     masked step still cuts the carry, as done_t cuts it everywhere else).
+ * An unmasked step followed by a masked one sees V_{t+1} of the masked token,
+ * as the plain GAE step does.  returns_t = A_t + V_t at every step.
+ */
+int ora_gae_skip(int64_t E, int64_t T, const float* rewards, const float* values,
+                 const float* terminateds, const float* truncateds,
+                 const float* bootstrap_values, const float* last_value, const float* skip,
+                 double gamma, double lambda, double* adv, double* ret) {
+    if (E < 0 || T < 0 || !rewards || !values || !terminateds || !skip || !adv) return -1;
+    if (last_value && (bootstrap_values || truncateds)) return -1;
+    const int has_trunc = truncateds != NULL;
+    for (int64_t e = 0; e < E; ++e) {
+        double a_next = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const int64_t i = IDX(e, t);
+            const double done = done_at(terminateds, truncateds, i);
+            const double v = (double)values[i];
+            double a;
+            if (skip[i] != 0.0f) {
+                a = (1.0 - done) * a_next;
+            } else {
+                const double term = (double)terminateds[i];
+                const double trunc = flag_or(truncateds, i);
+                double v_next = boot_at(bootstrap_values, last_value, has_trunc, e, t, T);
+                if (t < T - 1) v_next += (1.0 - trunc) * (double)values[i + 1];
+                const double delta = (double)rewards[i] + gamma * (1.0 - term) * v_next - v;
+                a = delta + gamma * lambda * (1.0 - done) * a_next;
+            }
+            adv[i] = a;
+            if (ret) ret[i] = a + v;
+            a_next = a;
+        }
+    }
+    return 0;
+}
+
+/*
  * V-trace  ([K] compute_vtrace Recurrence and Outputs; [P] Sec. 3.3.2, Table 1).
  *   rho_hat_t = exp(log pi_t - log mu_t);  rho_t = min(rho_bar, rho_hat_t);
  *   c_t = min(c_bar, rho_hat_t)

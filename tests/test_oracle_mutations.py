@@ -40,6 +40,15 @@ MUTATIONS = [
      ["gae"]),
     ("gae_layout_transposed", "ora_gae",
      "const int64_t i = IDX(e, t);", "const int64_t i = t * E + e;", ["gae"]),
+    ("skip_mask_inverted", "ora_gae_skip",
+     "if (skip[i] != 0.0f) {", "if (skip[i] == 0.0f) {", ["gae_skip"]),
+    ("skip_carry_ignores_done", "ora_gae_skip",
+     "a = (1.0 - done) * a_next;", "a = a_next;", ["gae_skip"]),
+    ("skip_carry_discounted", "ora_gae_skip",
+     "a = (1.0 - done) * a_next;", "a = gamma * lambda * (1.0 - done) * a_next;", ["gae_skip"]),
+    ("skip_masked_step_keeps_td_error", "ora_gae_skip",
+     "a = (1.0 - done) * a_next;",
+     "a = (double)rewards[i] - v + (1.0 - done) * a_next;", ["gae_skip"]),
     ("forward_layout_transposed", "ora_forward_scan",
      "const int64_t i = IDX(e, t);", "const int64_t i = t * E + e;", ["forward"]),
     ("vtrace_beta_uses_rho", "ora_vtrace",
@@ -80,6 +89,11 @@ def _checks(kind):
         yield lambda: pins.test_gae_every_flag_pattern(4)
         yield pins.test_gae_geometric_closed_form
         yield pins.test_window_bootstrap_enters_once
+    elif kind == "gae_skip":
+        yield lambda: pins.test_gae_skip_matches_textbook(0, "trunc_2d")
+        yield lambda: pins.test_gae_skip_matches_textbook(1, "none")
+        yield lambda: pins.test_gae_skip_equals_gae_on_the_row_without_masked_steps(0)
+        yield pins.test_gae_skip_episode_end_on_a_masked_step_cuts_the_carry
     elif kind == "vtrace":
         yield lambda: pins.test_vtrace_matches_episode_textbook(0, (0.8, 1.3), "trunc_2d")
         yield pins.test_vtrace_telescoping_sum

@@ -571,3 +571,94 @@ def test_synthetic_configs_are_well_formed():
     rt = synth.retrace_inputs(E=4, T=16, A=18)
     assert np.all(rt["actions"] >= 0) and np.all(rt["actions"] < 18)
     assert np.allclose(rt["pi_target"].sum(-1), 1.0, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# GAE with an observation-skip mask
+# ---------------------------------------------------------------------------
+
+def rand_skip(rng, E, T, p=0.35):
+    """Masked spans: each step starts or continues a span with probability p."""
+    return (rng.random((E, T)) < p).astype(np.float32)
+
+
+@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("mode", ["trunc_2d", "no_trunc_last_value", "none"])
+def test_gae_skip_matches_textbook(seed, mode):
+    rng = np.random.default_rng(300 + seed)
+    E, T = 3, 13
+    r, v, term, trunc, boot = rand_rollout(rng, E, T)
+    skip = rand_skip(rng, E, T)
+    kw = dict(gamma=0.97, lambda_=0.9)
+    if mode == "trunc_2d":
+        args = dict(truncateds=trunc, bootstrap_values=boot)
+    elif mode == "no_trunc_last_value":
+        args = dict(last_value=rng.standard_normal(E).astype(np.float32))
+    else:
+        args = {}
+    adv, ret = oracle.gae_skip(r, v, term, skip, **args, **kw)
+    want = tb.to_array(tb.gae_skip(r, v, term, skip, **args, **kw))
+    close(adv, want)
+    close(ret, want + v.astype(np.float64))
+
+
+def test_gae_skip_without_masked_steps_is_gae():
+    rng = np.random.default_rng(7)
+    r, v, term, trunc, boot = rand_rollout(rng, 4, 37)
+    a0, r0 = oracle.gae(r, v, term, trunc, 0.99, 0.95, boot)
+    a1, r1 = oracle.gae_skip(r, v, term, np.zeros_like(r), trunc, 0.99, 0.95, boot)
+    assert np.array_equal(a0, a1) and np.array_equal(r0, r1)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_gae_skip_equals_gae_on_the_row_without_masked_steps(seed):
+    """Insert masked spans (any rewards; values equal to the value of the next
+    unmasked step, 0 after the last one) into a row with terminations only:
+    the unmasked steps keep the advantages of the short row, and each masked
+    step holds the next unmasked step's advantage (0 after the last one)."""
+    rng = np.random.default_rng(50 + seed)
+    n = 17
+    r = rng.standard_normal(n).astype(np.float32)
+    v = rng.standard_normal(n).astype(np.float32)
+    term = (rng.random(n) < 0.15).astype(np.float32)
+    short, _ = oracle.gae(r[None], v[None], term[None], None, 0.98, 0.93)
+    R, V, TE, SK, where = [], [], [], [], []
+    for k in range(n):
+        for _ in range(rng.integers(0, 3)):          # masked span before step k
+            R.append(rng.standard_normal()); V.append(v[k]); TE.append(0.0); SK.append(1.0)
+        where.append(len(R))
+        R.append(r[k]); V.append(v[k]); TE.append(term[k]); SK.append(0.0)
+    for _ in range(2):                               # masked tail
+        R.append(rng.standard_normal()); V.append(0.0); TE.append(0.0); SK.append(1.0)
+    f = lambda x: np.asarray(x, np.float32)[None]
+    long_adv, _ = oracle.gae_skip(f(R), f(V), f(TE), f(SK), None, 0.98, 0.93)
+    close(long_adv[0, where], short[0])
+    nxt = 0.0
+    for i in range(len(R) - 1, -1, -1):
+        if SK[i]:
+            assert long_adv[0, i] == nxt
+        else:
+            nxt = long_adv[0, i]
+
+
+def test_gae_skip_fully_masked_row_is_zero():
+    rng = np.random.default_rng(1)
+    r, v, term, _, _ = rand_rollout(rng, 2, 9)
+    adv, ret = oracle.gae_skip(r, v, term, np.ones_like(r), None, 0.99, 0.95,
+                               last_value=np.ones(2, np.float32))
+    assert np.all(adv == 0.0)
+    close(ret, v)
+
+
+def test_gae_skip_episode_end_on_a_masked_step_cuts_the_carry():
+    T = 8
+    r = np.zeros((1, T), np.float32)
+    v = np.zeros((1, T), np.float32)
+    term = np.zeros((1, T), np.float32)
+    skip = np.zeros((1, T), np.float32)
+    skip[0, 3] = 1.0
+    term[0, 3] = 1.0                  # the episode ends on the masked step
+    r[0, 5] = 1.0                     # a reward in the next episode
+    adv, _ = oracle.gae_skip(r, v, term, skip, None, 0.9, 0.8)
+    assert np.all(adv[0, :4] == 0.0)
+    assert adv[0, 5] == 1.0 and adv[0, 4] == pytest.approx(0.9 * 0.8)

@@ -89,6 +89,36 @@ def gae(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
     return adv
 
 
+def gae_skip(rewards, values, terminateds, skip, truncateds=None, gamma=0.99, lambda_=0.95,
+             bootstrap_values=None, last_value=None):
+    """GAE when masked tokens (skip = 1) are transparent: inside each episode,
+    A_t = sum over unmasked k >= t of (gamma lambda)^n(t,k) delta_k, where
+    n(t,k) counts the unmasked steps j with t <= j < k.  A masked step adds no
+    TD error and no discount; episode ends cut wherever they are flagged."""
+    E, T = rewards.shape
+    g, gl = fr(gamma), fr(gamma) * fr(lambda_)
+    bf = _boot_fn(bootstrap_values, last_value, truncateds, T)
+    adv = [[None] * T for _ in range(E)]
+    for e in range(E):
+        done_row = [_done(terminateds, truncateds, e, t) for t in range(T)]
+        for s, end in episodes_backward(done_row):
+            delta = {}
+            for k in range(s, end + 1):
+                if skip[e, k] != 0:
+                    continue
+                inside = fr(values[e, k + 1]) if k + 1 < T else None
+                vs = _successor_value(e, k, T, terminateds, truncateds, bf, inside)
+                delta[k] = fr(rewards[e, k]) + g * vs - fr(values[e, k])
+            for t in range(s, end + 1):
+                total, n = F(0), 0
+                for k in range(t, end + 1):
+                    if k in delta:
+                        total += gl ** n * delta[k]
+                        n += 1
+                adv[e][t] = total
+    return adv
+
+
 def vtrace(log_rho, values, rewards, terminateds, truncateds=None, gamma=0.99, rho_bar=1.0,
            c_bar=1.0, bootstrap_values=None, last_value=None):
     """vs_t = V_t + sum_k gamma^{k-t} (prod_{i=t}^{k-1} c_i) rho_k delta_k per episode;
