@@ -166,6 +166,26 @@ rlscan_status rlscan_gae(const float* rewards, const float* values, const float*
                          void* ws, size_t ws_bytes, rlscan_stream_t stream);
 
 /*
+ * GAE with an observation-skip mask -- paper Sec. 9.3 (multi-turn and
+ * tool-use rows: the recurrence is carried across masked tokens, beta_t = 1).
+ * skip_mask: [E,T] float, nonzero = masked (an observation or tool-output
+ * token), or NULL (no masked steps: the same results as rlscan_gae).
+ * Unmasked steps are the rlscan_gae step.  A masked step adds no TD error and
+ * no discount: A_t = (1 - done_t) A_{t+1} (0 at the row end), so inside an
+ * episode it holds the advantage of the next unmasked step.  An episode end
+ * flagged on a masked step still cuts the carry, and a bootstrap value at a
+ * masked step is not used.  An unmasked step followed by a masked one uses
+ * V_{t+1} of the masked token, as in rlscan_gae.  returns_t = A_t + V_t at
+ * every step.  Other arguments, NULL rules, conflicts and errors are those of
+ * rlscan_gae.
+ */
+rlscan_status rlscan_gae_skip(const float* rewards, const float* values, const float* terminateds,
+                              const float* truncateds, const float* bootstrap_values,
+                              const float* last_value, const float* skip_mask, float* advantages,
+                              float* returns, int64_t num_envs, int64_t seq_len, float gamma,
+                              float lambda, void* ws, size_t ws_bytes, rlscan_stream_t stream);
+
+/*
  * GAE over the compact rollout format -- the recurrence of rlscan_gae (same
  * sources), with bf16 storage: rewards, values, bootstrap_values,
  * last_value, advantages and returns are bfloat16 (raw 16-bit patterns in

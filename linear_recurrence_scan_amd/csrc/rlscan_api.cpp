@@ -266,11 +266,12 @@ rlscan_status rlscan_check_inputs(const float* terminateds, const float* truncat
     return RLSCAN_OK;
 }
 
-rlscan_status rlscan_gae(const float* rewards, const float* values, const float* terminateds,
-                         const float* truncateds, const float* bootstrap_values,
-                         const float* last_value, float* advantages, float* returns,
-                         int64_t num_envs, int64_t seq_len, float gamma, float lambda, void* ws,
-                         size_t ws_bytes, rlscan_stream_t stream) {
+namespace {
+rlscan_status gae_call(const float* rewards, const float* values, const float* terminateds,
+                       const float* truncateds, const float* bootstrap_values,
+                       const float* last_value, const float* skip, float* advantages,
+                       float* returns, int64_t num_envs, int64_t seq_len, float gamma,
+                       float lambda, void* ws, size_t ws_bytes, rlscan_stream_t stream) {
     RLSCAN_TRY(check_shape(num_envs, seq_len));
     if (std::isnan(gamma) || std::isnan(lambda)) return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN");
     if (empty_batch(num_envs, seq_len)) return RLSCAN_OK;
@@ -284,13 +285,33 @@ rlscan_status rlscan_gae(const float* rewards, const float* values, const float*
         return set_error(RLSCAN_ERR_CONFLICT, "last_value cannot be combined with truncateds; use bootstrap_values");
     const bool vec = aligned16(rewards) && aligned16(values) && aligned16(terminateds) &&
                      aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(advantages) &&
-                     aligned16(returns);
+                     aligned16(returns) && aligned16(skip);
     Plan plan;
     RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
     RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
     GaeArgs a{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
-              advantages, returns, gamma, lambda};
+              advantages, returns, gamma, lambda, skip};
     return launch_gae(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
+}
+}  // namespace
+
+rlscan_status rlscan_gae(const float* rewards, const float* values, const float* terminateds,
+                         const float* truncateds, const float* bootstrap_values,
+                         const float* last_value, float* advantages, float* returns,
+                         int64_t num_envs, int64_t seq_len, float gamma, float lambda, void* ws,
+                         size_t ws_bytes, rlscan_stream_t stream) {
+    return gae_call(rewards, values, terminateds, truncateds, bootstrap_values, last_value, nullptr,
+                    advantages, returns, num_envs, seq_len, gamma, lambda, ws, ws_bytes, stream);
+}
+
+rlscan_status rlscan_gae_skip(const float* rewards, const float* values, const float* terminateds,
+                              const float* truncateds, const float* bootstrap_values,
+                              const float* last_value, const float* skip_mask, float* advantages,
+                              float* returns, int64_t num_envs, int64_t seq_len, float gamma,
+                              float lambda, void* ws, size_t ws_bytes, rlscan_stream_t stream) {
+    return gae_call(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+                    skip_mask, advantages, returns, num_envs, seq_len, gamma, lambda, ws, ws_bytes,
+                    stream);
 }
 
 rlscan_status rlscan_gae_bf16(const uint16_t* rewards, const uint16_t* values,

@@ -16,6 +16,7 @@ struct GaeArgs {
     const float *rewards, *values, *terminateds, *truncateds, *bootstrap_values, *last_value;
     float *advantages, *returns;
     float gamma, lambda;
+    const float* skip;  // observation-skip mask, or null
 };
 
 // Compact rollout format: bf16 values (raw 16-bit storage), one-byte flags.
@@ -72,6 +73,7 @@ constexpr int kShortRowTile = 2048;
 constexpr int kShortRowWaves = 4;
 
 rlscan_status launch_gae(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
+rlscan_status launch_gae_skip(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_gae_compact(const GaeCompactArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_vtrace(const VtraceArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s);

@@ -42,6 +42,7 @@ enum : unsigned {
     kNextValues = 4u,    // TD(lambda) next_values given
     kLogpBehavior = 8u,  // V-trace log_pi_behavior given
     kSameClip = 16u,     // V-trace rho_bar == c_bar
+    kSkip = 32u,         // GAE observation-skip mask given
 };
 
 struct SegInfo {

@@ -75,6 +75,7 @@ def _declare(L):
     L.rlscan_workspace_init.argtypes = [vp, sz, vp]
     L.rlscan_workspace_error.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     L.rlscan_gae.argtypes = [vp] * 8 + [i64, i64, f32, f32, vp, sz, vp]
+    L.rlscan_gae_skip.argtypes = [vp] * 9 + [i64, i64, f32, f32, vp, sz, vp]
     L.rlscan_gae_bf16.argtypes = [vp] * 8 + [i64, i64, f32, f32, vp, sz, vp]
     L.rlscan_vtrace.argtypes = [vp] * 10 + [i64, i64, f32, f32, f32, vp, sz, vp]
     L.rlscan_retrace.argtypes = [vp] * 10 + [i64, i64, i64, f32, f32, f32, f32, vp, sz, vp]
@@ -86,7 +87,7 @@ def _declare(L):
     L.rlscan_check_inputs.argtypes = [vp] * 4 + [i64, i64, i64, vp, sz,
                                                  ctypes.POINTER(CheckReport), vp]
     for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
-                 "rlscan_gae", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
+                 "rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
                  "rlscan_check_inputs", "rlscan_debug_set_launch_shape",
                  "rlscan_debug_set_lookback_jitter"):
         getattr(L, name).restype = st
@@ -235,6 +236,18 @@ def rlscan_gae(rewards, values, terminateds, truncateds, bootstrap_values, last_
     _check("rlscan_gae", st)
 
 
+def rlscan_gae_skip(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+                    skip_mask, advantages, returns, gamma, lambda_):
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    ws, nws = workspace(dev, E, T)
+    st = lib().rlscan_gae_skip(_ptr(rewards), _ptr(values), _ptr(terminateds), _ptr(truncateds),
+                               _ptr(bootstrap_values), _ptr(last_value), _ptr(skip_mask),
+                               _ptr(advantages), _ptr(returns), E, T, float(gamma), float(lambda_),
+                               _ptr(ws), nws, _stream(dev))
+    _check("rlscan_gae_skip", st)
+
+
 def rlscan_gae_bf16(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
                     advantages, returns, gamma, lambda_):
     E, T = _shape2("rewards", rewards)
@@ -319,8 +332,10 @@ def rlscan_debug_wave_scan(a, b, out_a, out_b):
 # ---------------------------------------------------------------------------
 
 def gae(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
-        bootstrap_values=None, last_value=None, want_returns=False):
-    """GAE advantages (and returns = advantages + values if want_returns)."""
+        bootstrap_values=None, last_value=None, want_returns=False, skip_mask=None):
+    """GAE advantages (and returns = advantages + values if want_returns).
+    skip_mask (float32 [E,T], 1 = observation token): masked steps carry the
+    recurrence (no TD error, no discount)."""
     E, T = _shape2("rewards", rewards)
     dev = rewards.device
     r = _f32("rewards", rewards, (E, T))
@@ -329,10 +344,14 @@ def gae(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
     tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
     bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
     lv = _f32("last_value", last_value, (E,), dev, optional=True)
+    sk = _f32("skip_mask", skip_mask, (E, T), dev, optional=True)
     _debug_check("gae", terminateds=te, truncateds=tr, bootstrap_values=bv)
     adv = torch.empty_like(r)
     ret = torch.empty_like(r) if want_returns else None
-    rlscan_gae(r, v, te, tr, bv, lv, adv, ret, gamma, lambda_)
+    if sk is None:
+        rlscan_gae(r, v, te, tr, bv, lv, adv, ret, gamma, lambda_)
+    else:
+        rlscan_gae_skip(r, v, te, tr, bv, lv, sk, adv, ret, gamma, lambda_)
     return (adv, ret) if want_returns else adv
 
 

@@ -165,3 +165,18 @@ def forward_inputs(E, T, seed, p_done=0.01, seeded=True):
     dones = (rng.random((E, T)) < p_done).astype(np.float32)
     seed_v = rng.standard_normal(E).astype(np.float32) if seeded else None
     return {"inputs": x, "dones": dones, "seed_values": seed_v}
+
+
+def skip_spans(E, T, seed, p_enter=0.02, p_leave=1.0 / 16):
+    """Observation-skip mask of a multi-turn row: a two-state chain per row that
+    enters a masked span with probability p_enter per step and leaves it with
+    probability p_leave (mean span 16 steps); 1.0 = masked.  Rows start
+    unmasked."""
+    rng = _rng(seed)
+    u = rng.random((E, T))
+    out = np.zeros((E, T), np.float32)
+    state = np.zeros(E, bool)
+    for t in range(T):
+        state = np.where(state, u[:, t] >= p_leave, u[:, t] < p_enter)
+        out[:, t] = state
+    return out

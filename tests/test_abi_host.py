@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
-    for n in ("rlscan_gae", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
+    for n in ("rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
         assert n in names
 
 
@@ -81,6 +81,19 @@ def test_gae_validation(L):
     assert gae(L, lv=P, bv=P) == CONFLICT
     assert gae(L, lv=P, tr=P) == CONFLICT
     assert L.rlscan_gae(P, P, P, N, N, N, P, N, 4, 8, float("nan"), 0.95, N, 0, N) == BAD_PARAM
+
+
+def test_gae_skip_validation(L):
+    def call(r=P, v=P, te=P, tr=N, bv=N, lv=N, sk=P, adv=P, ret=N, E=4, T=8, g=0.99):
+        return L.rlscan_gae_skip(r, v, te, tr, bv, lv, sk, adv, ret, E, T, g, 0.95, N, 0, N)
+    for kw in ("r", "v", "te", "adv"):
+        assert call(**{kw: N}) == NULL_ARG, kw
+    assert call(E=0) == OK
+    assert call(T=-1) == BAD_SHAPE
+    assert call(lv=P, bv=P) == CONFLICT
+    assert call(lv=P, tr=P) == CONFLICT
+    assert call(g=float("nan")) == BAD_PARAM
+    assert call(E=4096, T=1000) == WORKSPACE
 
 
 def test_gae_bf16_validation(L):
