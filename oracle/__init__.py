@@ -55,7 +55,8 @@ def configure(lib):
     lib.ora_lambda_returns.argtypes = [i64, i64, vp, vp, vp, vp, vp, dbl, dbl, vp]
     lib.ora_discounted_returns.argtypes = [i64, i64, vp, vp, vp, vp, dbl, vp]
     lib.ora_forward_scan.argtypes = [i64, i64, vp, vp, vp, dbl, ctypes.c_int, vp]
-    for name in ("ora_gae", "ora_gae_skip", "ora_vtrace", "ora_retrace", "ora_lambda_returns",
+    lib.ora_traces_vec.argtypes = [i64, i64, i64, vp, vp, vp, vp, dbl, vp]
+    for name in ("ora_traces_vec", "ora_gae", "ora_gae_skip", "ora_vtrace", "ora_retrace", "ora_lambda_returns",
                  "ora_discounted_returns", "ora_forward_scan"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -221,3 +222,21 @@ def eligibility_traces(gradients, dones, gamma, lambda_, seed_values=None, decay
 def episodic_prefix_sum(inputs, dones, seed_values=None, boundary="ends_at"):
     """Cumulative sum that resets at segment boundaries (decay 1)."""
     return forward_scan(inputs, dones, seed_values, 1.0, boundary)
+
+
+def traces_vec(gradients, dones, kappa=1.0, decay=None, seed_values=None):
+    """Vector eligibility traces z_t[d] = g_t[d] + b_t[d] (1 - done_{t-1}) z_{t-1}[d]
+    over [E,T,D] gradients (b = decay[E,T,D], or the scalar kappa), float64."""
+    g = np.asarray(gradients)
+    if g.ndim != 3:
+        raise ValueError("expected [num_envs, seq_len, dim] gradients")
+    E, T, D = g.shape
+    g = _f32(g, (E, T, D))
+    dc = _f32(decay, (E, T, D))
+    dn = _f32(dones, (E, T))
+    s = _f32(seed_values, (E, D))
+    out = np.empty((E, T, D), np.float64)
+    rc = _load().ora_traces_vec(E, T, D, _ptr(g), _ptr(dc), _ptr(dn), _ptr(s), float(kappa),
+                                _ptr(out))
+    _check(rc, "traces_vec")
+    return out

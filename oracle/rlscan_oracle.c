@@ -341,3 +341,34 @@ int ora_forward_scan(int64_t E, int64_t T, const float* inputs, const float* don
     }
     return 0;
 }
+
+/*
+ * Vector eligibility traces with per-dimension decay ([S] Eligibility Traces,
+ * Definition: z_t = g_t + gamma lambda (1 - d_{t-1}) z_{t-1}, here for a
+ * vector g_t of D entries; [P] Sec. 8 names per-dimension beta, as true online
+ * TD(lambda) and per-parameter traces need, as outside its kernels' scalar-beta
+ * structure).  For every env e and dimension d, in time order:
+ *   z_t[d] = g_t[d] + b_t[d] (1 - done_{t-1}) z_{t-1}[d],
+ *   z_{-1}[d] = seed[e,d] (or 0),  done_{-1} = 0,
+ * with b_t[d] = decay[e,t,d] when a decay array is given, else the scalar
+ * kappa (gamma lambda) for every entry.  gradients, decay and out are
+ * [E,T,D] row-major (D fastest); dones is [E,T]; seed is [E,D].
+ */
+int ora_traces_vec(int64_t E, int64_t T, int64_t D, const float* gradients, const float* decay,
+                   const float* dones, const float* seed, double kappa, double* out) {
+    if (E < 0 || T < 0 || D < 0 || !gradients || !dones || !out) return -1;
+    for (int64_t e = 0; e < E; ++e) {
+        for (int64_t d = 0; d < D; ++d) {
+            double z = seed ? (double)seed[e * D + d] : 0.0;
+            double d_prev = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t i = (e * T + t) * D + d;
+                const double b = decay ? (double)decay[i] : kappa;
+                z = (double)gradients[i] + b * (1.0 - d_prev) * z;
+                out[i] = z;
+                d_prev = (double)dones[e * T + t];
+            }
+        }
+    }
+    return 0;
+}

@@ -49,6 +49,15 @@ MUTATIONS = [
     ("skip_masked_step_keeps_td_error", "ora_gae_skip",
      "a = (1.0 - done) * a_next;",
      "a = (double)rewards[i] - v + (1.0 - done) * a_next;", ["gae_skip"]),
+    ("traces_vec_gate_on_current_done", "ora_traces_vec",
+     "d_prev = (double)dones[e * T + t];", "d_prev = 0.0;", ["traces_vec"]),
+    ("traces_vec_decay_index_t_minus_1", "ora_traces_vec",
+     "const double b = decay ? (double)decay[i] : kappa;",
+     "const double b = decay ? (double)decay[t > 0 ? i - D : i] : kappa;", ["traces_vec"]),
+    ("traces_vec_seed_ignored", "ora_traces_vec",
+     "double z = seed ? (double)seed[e * D + d] : 0.0;", "double z = 0.0;", ["traces_vec"]),
+    ("traces_vec_seed_transposed", "ora_traces_vec",
+     "(double)seed[e * D + d]", "(double)seed[d * E + e]", ["traces_vec"]),
     ("forward_layout_transposed", "ora_forward_scan",
      "const int64_t i = IDX(e, t);", "const int64_t i = t * E + e;", ["forward"]),
     ("vtrace_beta_uses_rho", "ora_vtrace",
@@ -94,6 +103,10 @@ def _checks(kind):
         yield lambda: pins.test_gae_skip_matches_textbook(1, "none")
         yield lambda: pins.test_gae_skip_equals_gae_on_the_row_without_masked_steps(0)
         yield pins.test_gae_skip_episode_end_on_a_masked_step_cuts_the_carry
+    elif kind == "traces_vec":
+        yield lambda: pins.test_traces_vec_match_textbook(0, True, True)
+        yield lambda: pins.test_traces_vec_match_textbook(1, False, True)
+        yield pins.test_traces_vec_done_resets_every_dimension
     elif kind == "vtrace":
         yield lambda: pins.test_vtrace_matches_episode_textbook(0, (0.8, 1.3), "trunc_2d")
         yield pins.test_vtrace_telescoping_sum

@@ -662,3 +662,66 @@ def test_gae_skip_episode_end_on_a_masked_step_cuts_the_carry():
     adv, _ = oracle.gae_skip(r, v, term, skip, None, 0.9, 0.8)
     assert np.all(adv[0, :4] == 0.0)
     assert adv[0, 5] == 1.0 and adv[0, 4] == pytest.approx(0.9 * 0.8)
+
+
+# ---------------------------------------------------------------------------
+# Vector eligibility traces with per-dimension decay
+# ---------------------------------------------------------------------------
+
+def rand_traces(rng, E, T, D, p_done=0.2):
+    g = rng.standard_normal((E, T, D)).astype(np.float32)
+    decay = rng.uniform(0.0, 1.2, (E, T, D)).astype(np.float32)
+    dones = (rng.random((E, T)) < p_done).astype(np.float32)
+    seed = rng.standard_normal((E, D)).astype(np.float32)
+    return g, decay, dones, seed
+
+
+@pytest.mark.parametrize("seed", range(5))
+@pytest.mark.parametrize("with_decay", [True, False])
+@pytest.mark.parametrize("with_seed", [True, False])
+def test_traces_vec_match_textbook(seed, with_decay, with_seed):
+    rng = np.random.default_rng(400 + seed)
+    E, T, D = 2, 9, 3
+    g, decay, dones, sv = rand_traces(rng, E, T, D)
+    kappa = np.float32(0.9405)
+    got = oracle.traces_vec(g, dones, kappa, decay if with_decay else None,
+                            sv if with_seed else None)
+    want = tb.traces_vec(g, dones, decay if with_decay else kappa, sv if with_seed else None)
+    close(got, np.asarray(want, np.float64))
+
+
+def test_traces_vec_scalar_decay_columns_are_eligibility_traces():
+    """Without a decay array every dimension is the scalar-beta trace of the
+    forward oracle on that column."""
+    rng = np.random.default_rng(11)
+    E, T, D = 3, 50, 7
+    g, _, dones, sv = rand_traces(rng, E, T, D, p_done=0.05)
+    got = oracle.traces_vec(g, dones, np.float32(0.9), None, sv)
+    for d in range(D):
+        want = oracle.forward_scan(np.ascontiguousarray(g[:, :, d]), dones, sv[:, d], np.float32(0.9))
+        assert np.array_equal(got[:, :, d], want)
+
+
+def test_traces_vec_geometric_closed_form():
+    """Constant per-dimension decay b_d, constant input, no dones:
+    z_t = (1 - b^(t+1)) / (1 - b) for a zero seed."""
+    T, D = 40, 4
+    b = np.array([0.5, 0.9, 0.25, 0.75], np.float32)
+    g = np.ones((1, T, D), np.float32)
+    decay = np.broadcast_to(b, (1, T, D)).copy()
+    got = oracle.traces_vec(g, np.zeros((1, T), np.float32), 0.0, decay)
+    t = np.arange(T)[:, None]
+    want = (1.0 - b.astype(np.float64) ** (t + 1)) / (1.0 - b.astype(np.float64))
+    close(got[0], want)
+
+
+def test_traces_vec_done_resets_every_dimension():
+    rng = np.random.default_rng(3)
+    g, decay, _, sv = rand_traces(rng, 1, 12, 5)
+    dones = np.zeros((1, 12), np.float32)
+    dones[0, 6] = 1.0
+    got = oracle.traces_vec(g, dones, 0.0, decay, sv)
+    g2 = g.copy()
+    g2[:, :7] = 0.0                      # earlier inputs must not reach t >= 7
+    got2 = oracle.traces_vec(g2, dones, 0.0, decay, np.zeros_like(sv))
+    assert np.array_equal(got[0, 7:], got2[0, 7:])

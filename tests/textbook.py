@@ -262,5 +262,35 @@ def forward_segments(inputs, dones, seed_values, decay, boundary):
     return out
 
 
+def traces_vec(gradients, dones, decay, seed):
+    """Per dimension d, inside each episode [s, t] (s the first step after the
+    last done before t): z_t = sum_{k=s}^{t} (prod_{j=k+1}^{t} b_j) g_k, plus
+    (prod_{j=0}^{t} b_j) seed when no done precedes t.  decay: [E,T,D] array b,
+    or a scalar for every entry."""
+    E, T, D = gradients.shape
+    out = np.empty((E, T, D), dtype=object)
+    for e in range(E):
+        for d in range(D):
+            b = [fr(decay[e, t, d]) if isinstance(decay, np.ndarray) else fr(decay)
+                 for t in range(T)]
+            s = 0
+            for t in range(T):
+                if t > 0 and dones[e, t - 1] != 0:
+                    s = t
+                total = F(0)
+                for k in range(s, t + 1):
+                    w = F(1)
+                    for j in range(k + 1, t + 1):
+                        w *= b[j]
+                    total += w * fr(gradients[e, k, d])
+                if s == 0 and seed is not None:
+                    w = F(1)
+                    for j in range(0, t + 1):
+                        w *= b[j]
+                    total += w * fr(seed[e, d])
+                out[e, t, d] = total
+    return out
+
+
 def to_array(rows):
     return np.array([[float(x) for x in row] for row in rows], dtype=np.float64)
