@@ -345,7 +345,7 @@ int ora_forward_scan(int64_t E, int64_t T, const float* inputs, const float* don
 /*
  * Vector eligibility traces with per-dimension decay ([S] Eligibility Traces,
  * Definition: z_t = g_t + gamma lambda (1 - d_{t-1}) z_{t-1}, here for a
- * vector g_t of D entries; [P] Sec. 8 names per-dimension beta, as true online
+ * vector g_t of D entries; [P] Sec. 9.2 names per-dimension beta, as true online
  * TD(lambda) and per-parameter traces need, as outside its kernels' scalar-beta
  * structure).  For every env e and dimension d, in time order:
  *   z_t[d] = g_t[d] + b_t[d] (1 - done_{t-1}) z_{t-1}[d],
