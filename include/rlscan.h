@@ -166,6 +166,30 @@ rlscan_status rlscan_gae(const float* rewards, const float* values, const float*
                          void* ws, size_t ws_bytes, rlscan_stream_t stream);
 
 /*
+ * Vector eligibility traces with per-dimension decay -- returns/traces page,
+ * Eligibility Traces (Definition: z_t = g_t + gamma lambda (1 - d_{t-1})
+ * z_{t-1}) for a vector input; per-dimension beta is what paper Sec. 9.2
+ * names as beyond a scalar-beta kernel (true online TD(lambda),
+ * per-parameter traces).  For every env e, dimension d and step t:
+ *   z_t[d] = g_t[d] + b_t[d] (1 - done_{t-1}) z_{t-1}[d],  z_{-1} = seed[e,d] (or 0),
+ *   done_{-1} = 0,  b = decay[e,t,d], or kappa (e.g. gamma*lambda) when decay is NULL.
+ * Inputs  gradients [E,T,D] (D fastest), decay [E,T,D] or NULL, dones [E,T]
+ *         (exactly 0/1), seed [E,D] or NULL.
+ * Output  traces [E,T,D].
+ * Workspace: rlscan_traces_vec_workspace_bytes(E,T,D) bytes (0 when T fits
+ *         one tile of 64 steps), zeroed once with rlscan_workspace_init; the
+ *         same workspace may serve the other entry points of one stream.
+ * Errors  NULL gradients/dones/traces -> NULL_ARG; E, T or D < 0, T or D >=
+ *         2^31, E*T*D > 2^46 -> BAD_SHAPE; kappa NaN -> BAD_PARAM; missing,
+ *         misaligned or small workspace -> WORKSPACE.  E, T or D = 0 -> OK.
+ */
+rlscan_status rlscan_traces_vec(const float* gradients, const float* decay, const float* dones,
+                                const float* seed, float* traces, int64_t num_envs,
+                                int64_t seq_len, int64_t dim, float kappa, void* ws,
+                                size_t ws_bytes, rlscan_stream_t stream);
+size_t rlscan_traces_vec_workspace_bytes(int64_t num_envs, int64_t seq_len, int64_t dim);
+
+/*
  * GAE with an observation-skip mask -- paper Sec. 9.3 (multi-turn and
  * tool-use rows: the recurrence is carried across masked tokens, beta_t = 1).
  * skip_mask: [E,T] float, nonzero = masked (an observation or tool-output

@@ -1,0 +1,316 @@
+// op_traces_vec.hip -- eligibility traces over a vector input with
+// per-dimension decay (returns/traces page, Eligibility Traces, Definition:
+// z_t = g_t + gamma lambda (1 - d_{t-1}) z_{t-1}; paper Sec. 9.2 names
+// per-dimension beta, which true online TD(lambda) and per-parameter traces
+// need, as outside a scalar-beta kernel):
+//   z_t[d] = g_t[d] + b_t[d] (1 - done_{t-1}) z_{t-1}[d],  z_{-1} = seed, done_{-1} = 0
+// over [E,T,D] arrays (D fastest), b = decay[E,T,D] or the scalar kappa.
+//
+// Layout.  Every (env, dim) pair is an independent column scanned along t
+// with stride D.  A lane owns G consecutive columns (G = 4 with 16-byte
+// accesses when D % 4 == 0 and the arrays are 16-byte aligned), so a wave's
+// access at one step covers 64*G consecutive floats of a row.  A workgroup of
+// W waves takes a tile of 64 column groups by W*S steps; wave w holds steps
+// [w*S, (w+1)*S) of it in registers.
+//   1. every wave loads its S steps and folds them per lane into one affine
+//      map (a, b) per column: z_out = a + b * z_in;
+//   2. the W maps meet in LDS; each wave composes the ones before it;
+//   3. wave 0 finds the value entering the tile: the seed for the first
+//      chunk of t, else a decoupled look-back over the earlier chunks of the
+//      same columns, through 64-bit words that each carry one column's value
+//      and an epoch tag (aggregate 2e+1, inclusive 2e+2), so a word is valid
+//      or not by itself and needs no fence;
+//   4. every wave replays its S steps from its entering value and stores z.
+// Tiles run chunk-major (blockIdx = chunk * column_blocks + column_block), so
+// a tile waits only on tiles with smaller blockIdx, which were dispatched
+// before it: the lowest unfinished tile can always finish.
+#include <hip/hip_runtime.h>
+
+#include "rlscan_internal.hpp"
+#include "scan_core.hpp"
+
+namespace rlscan {
+
+namespace {
+
+constexpr int kVecS = 8;  // steps per wave
+constexpr int kVecW = 8;  // waves per workgroup
+
+struct VecGeo {
+    int64_t E, T, D;
+    int64_t col_groups;  // E*D / G
+    int64_t col_blocks;  // ceil(col_groups / 64)
+    int64_t chunks;      // ceil(T / (W*S))
+    int64_t num_tiles;   // chunks * col_blocks
+    uint32_t jitter;
+};
+
+// Word (which: 0 = aggregate a, 1 = aggregate b, 2 = inclusive) of column
+// j of `lane` in tile q.  Consecutive lanes hold consecutive words.
+template <int G>
+__device__ __forceinline__ uint64_t* vec_word(uint8_t* ws, int64_t q, int which, int j, int lane) {
+    uint64_t* slots = reinterpret_cast<uint64_t*>(ws + WsHeader::kSlotsByteOffset);
+    return slots + (((q * 3 + which) * G + j) * 64 + lane);
+}
+
+template <int G>
+__device__ __forceinline__ void load_g(const float* p, bool ok, float (&out)[G]) {
+    if constexpr (G == 4) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (ok) v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
+    } else {
+        out[0] = ok ? __builtin_nontemporal_load(p) : 0.f;
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void store_g(float* p, const float (&in)[G]) {
+    if constexpr (G == 4) {
+        f32x4 v;
+        v.x = in[0]; v.y = in[1]; v.z = in[2]; v.w = in[3];
+        *reinterpret_cast<f32x4*>(p) = v;
+    } else {
+        *p = in[0];
+    }
+}
+
+template <int G, int S, int W, bool DECAY>
+__global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecGeo g, uint8_t* ws) {
+    __shared__ float sh_a[W][G][64];
+    __shared__ float sh_b[W][G][64];
+    __shared__ float sh_carry[G][64];
+
+    const int64_t q = blockIdx.x;
+    const int64_t k = q / g.col_blocks;
+    const int64_t cb = q - k * g.col_blocks;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / 64));
+    const int lane = lane_id();
+    const int64_t cgi = cb * 64 + lane;
+    const bool active = cgi < g.col_groups;
+    const int64_t col = (active ? cgi : 0) * G;
+    const int64_t e = col / g.D;
+    const int64_t d0 = col - e * g.D;
+    const int64_t t0 = k * (int64_t)(W * S) + (int64_t)wave * S;
+    const bool lookback = g.chunks > 1;
+
+    uint64_t ticket = 0;
+    if (lookback && wave == 0 && lane == 0) ticket = epoch_ticket(ws, q);
+
+    // 1. loads: gradient, decay and the previous step's done flag per step
+    const int64_t off0 = (e * g.T + t0) * g.D + d0;
+    float gv[S][G], bv[S][G];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int64_t t = t0 + s;
+        const bool ok = active && t < g.T;
+        load_g<G>(p.gradients + off0 + s * g.D, ok, gv[s]);
+        float dec[G];
+        if constexpr (DECAY) {
+            load_g<G>(p.decay + off0 + s * g.D, ok, dec);
+        } else {
+#pragma unroll
+            for (int j = 0; j < G; ++j) dec[j] = p.kappa;
+        }
+        const float gate = (ok && t > 0) ? 1.f - p.dones[e * g.T + t - 1] : 1.f;
+#pragma unroll
+        for (int j = 0; j < G; ++j) bv[s][j] = ok ? dec[j] * gate : 1.f;  // identity past T
+    }
+
+    float A[G], B[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        A[j] = 0.f;
+        B[j] = 1.f;
+    }
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            A[j] = fmaf(bv[s][j], A[j], gv[s][j]);
+            B[j] *= bv[s][j];
+        }
+
+    // 2. wave maps meet in LDS
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        sh_a[wave][j][lane] = A[j];
+        sh_b[wave][j][lane] = B[j];
+    }
+    __syncthreads();
+    float XA[G], XB[G];  // composition of the waves before this one
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+        XA[j] = 0.f;
+        XB[j] = 1.f;
+    }
+    for (int w = 0; w < wave; ++w)
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const float b = sh_b[w][j][lane];
+            XA[j] = fmaf(b, XA[j], sh_a[w][j][lane]);
+            XB[j] *= b;
+        }
+
+    // 3. the value entering the tile (wave 0)
+    if (wave == 0) {
+        float TA[G], TB[G];  // the whole tile's map
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            TA[j] = XA[j];
+            TB[j] = XB[j];
+        }
+        for (int w = 0; w < W; ++w)
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const float b = sh_b[w][j][lane];
+                TA[j] = fmaf(b, TA[j], sh_a[w][j][lane]);
+                TB[j] *= b;
+            }
+        float carry[G];
+        if (k == 0) {
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                carry[j] = (p.seed && active) ? p.seed[e * g.D + d0 + j] : 0.f;
+        }
+        if (lookback) {
+            const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)ticket, 0);
+            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(ticket >> 32), 0);
+            const uint64_t tk = ((uint64_t)hi << 32) | lo;
+            if (lane == 0) epoch_advance(ws, q, g.num_tiles, tk);
+            const uint32_t epoch = hi;
+            const uint32_t tag_agg = 2u * epoch + 1u, tag_inc = 2u * epoch + 2u;
+            if (g.jitter) jitter_delay(g.jitter, q);
+            if (k == 0) {
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+                    slot_store(vec_word<G>(ws, q, 2, j, lane), tag_inc, fmaf(TB[j], carry[j], TA[j]));
+            } else {
+                // a column whose map ignores its input publishes its
+                // inclusive value at once, the others their aggregate
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    if (TB[j] == 0.f) {
+                        slot_store(vec_word<G>(ws, q, 2, j, lane), tag_inc, TA[j]);
+                    } else {
+                        slot_store(vec_word<G>(ws, q, 0, j, lane), tag_agg, TA[j]);
+                        slot_store(vec_word<G>(ws, q, 1, j, lane), tag_agg, TB[j]);
+                    }
+                }
+                // Walk back to the nearest chunk with a published inclusive
+                // value (stepping over published aggregates), then apply the
+                // aggregates after it in scan order, x <- a_i + b_i * x: the
+                // same operations the tiles in between use for their own
+                // inclusive values, so the result is the same bits whichever
+                // inclusive value was found first.
+                int64_t jj[G];
+                bool found[G];
+#pragma unroll
+                for (int j = 0; j < G; ++j) {
+                    jj[j] = k - 1;
+                    found[j] = false;
+                    carry[j] = 0.f;
+                }
+                uint32_t spins = 0;
+                for (;;) {
+                    bool all = true;
+#pragma unroll
+                    for (int j = 0; j < G; ++j) {
+                        if (!found[j]) {
+                            const int64_t qj = jj[j] * g.col_blocks + cb;
+                            const uint64_t inc = slot_load(vec_word<G>(ws, qj, 2, j, lane));
+                            const uint64_t a = slot_load(vec_word<G>(ws, qj, 0, j, lane));
+                            const uint64_t b = slot_load(vec_word<G>(ws, qj, 1, j, lane));
+                            if (tag_of(inc) == tag_inc) {
+                                carry[j] = val_of(inc);
+                                found[j] = true;
+                            } else if (tag_of(a) == tag_agg && tag_of(b) == tag_agg) {
+                                --jj[j];  // chunk 0 publishes inclusive values only
+                            }
+                            all = all && found[j];
+                        }
+                    }
+                    if (__ballot(!all) == 0) break;
+                    if (++spins > kSpinLimit) {
+                        if (lane == 0)
+                            __hip_atomic_fetch_or(reinterpret_cast<uint32_t*>(ws) + WsHeader::kError, 1u,
+                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                        for (int j = 0; j < G; ++j)
+                            if (!found[j]) {
+                                carry[j] = 0.f;
+                                jj[j] = k - 1;
+                            }
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+                    for (int64_t i = jj[j] + 1; i < k; ++i) {  // aggregates seen published above
+                        const int64_t qi = i * g.col_blocks + cb;
+                        const float a = val_of(slot_load(vec_word<G>(ws, qi, 0, j, lane)));
+                        const float b = val_of(slot_load(vec_word<G>(ws, qi, 1, j, lane)));
+                        carry[j] = fmaf(b, carry[j], a);
+                    }
+#pragma unroll
+                for (int j = 0; j < G; ++j)
+                    if (TB[j] != 0.f)
+                        slot_store(vec_word<G>(ws, q, 2, j, lane), tag_inc, fmaf(TB[j], carry[j], TA[j]));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) sh_carry[j][lane] = carry[j];
+    }
+    __syncthreads();
+
+    // 4. replay the wave's steps from its entering value
+    float z[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j) z[j] = fmaf(XB[j], sh_carry[j][lane], XA[j]);
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+#pragma unroll
+        for (int j = 0; j < G; ++j) z[j] = fmaf(bv[s][j], z[j], gv[s][j]);
+        if (active && t0 + s < g.T) store_g<G>(p.traces + off0 + s * g.D, z);
+    }
+}
+
+template <int G, bool DECAY>
+rlscan_status launch_g(const VecTraceArgs& a, const VecGeo& g, void* ws, hipStream_t s) {
+    hipLaunchKernelGGL((traces_vec_kernel<G, kVecS, kVecW, DECAY>), dim3((unsigned)g.num_tiles),
+                       dim3(64 * kVecW), 0, s, a, g, static_cast<uint8_t*>(ws));
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
+    return RLSCAN_OK;
+}
+
+}  // namespace
+
+int64_t traces_vec_tiles(int64_t E, int64_t T, int64_t D, int G, int64_t* chunks) {
+    const int64_t groups = E * D / G;
+    const int64_t blocks = (groups + 63) / 64;
+    const int64_t steps = (int64_t)kVecW * kVecS;
+    const int64_t c = (T + steps - 1) / steps;
+    if (chunks) *chunks = c;
+    return blocks * c;
+}
+
+rlscan_status launch_traces_vec(const VecTraceArgs& a, int G, void* ws, uint32_t jitter,
+                                hipStream_t s) {
+    VecGeo g;
+    g.E = a.E;
+    g.T = a.T;
+    g.D = a.D;
+    g.col_groups = a.E * a.D / G;
+    g.col_blocks = (g.col_groups + 63) / 64;
+    g.num_tiles = traces_vec_tiles(a.E, a.T, a.D, G, &g.chunks);
+    g.jitter = jitter;
+    if (g.num_tiles >= ((int64_t)1 << 31))
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "too many tiles for one launch");
+    const bool decay = a.decay != nullptr;
+    if (G == 4) return decay ? launch_g<4, true>(a, g, ws, s) : launch_g<4, false>(a, g, ws, s);
+    return decay ? launch_g<1, true>(a, g, ws, s) : launch_g<1, false>(a, g, ws, s);
+}
+
+}  // namespace rlscan

@@ -141,6 +141,22 @@ rlscan_status check_shape(int64_t E, int64_t T) {
 
 bool empty_batch(int64_t E, int64_t T) { return E == 0 || T == 0; }
 
+// [E,T,D]: T < 2^31, D < 2^31, E*T*D <= 2^46.
+rlscan_status check_shape_vec(int64_t E, int64_t T, int64_t D) {
+    if (E < 0 || T < 0 || D < 0)
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs, seq_len and dim must be >= 0");
+    if (T >= ((int64_t)1 << 31) || D >= ((int64_t)1 << 31))
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "seq_len and dim must be < 2^31");
+    if (T > 0 && D > 0 &&
+        (E > ((int64_t)1 << 40) || E > (((int64_t)1 << 46) / T) / D))
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len * dim too large");
+    return RLSCAN_OK;
+}
+
+// Look-back words of one vector-trace tile: 3 per column, 64 lanes of up to 4
+// columns each (sized for 4 whatever the launch uses).
+constexpr size_t kVecWordsPerTile = 3 * 4 * 64;
+
 rlscan_status check_ws(const Plan& plan, void* ws, size_t ws_bytes) {
     if (!plan.lookback) return RLSCAN_OK;
     if (!ws) return set_error(RLSCAN_ERR_WORKSPACE, "this shape needs a workspace (rlscan_workspace_bytes)");
@@ -197,6 +213,16 @@ size_t rlscan_workspace_bytes(int64_t num_envs, int64_t seq_len) {
     if (check_shape(num_envs, seq_len) != RLSCAN_OK || empty_batch(num_envs, seq_len)) return 0;
     const int64_t N = num_envs * seq_len;
     return ws_bytes_for_tiles((N + kMinTile - 1) / kMinTile);
+}
+
+size_t rlscan_traces_vec_workspace_bytes(int64_t num_envs, int64_t seq_len, int64_t dim) {
+    if (check_shape_vec(num_envs, seq_len, dim) != RLSCAN_OK || num_envs == 0 || seq_len == 0 ||
+        dim == 0)
+        return 0;
+    int64_t chunks = 0;
+    const int64_t tiles = traces_vec_tiles(num_envs, seq_len, dim, 1, &chunks);
+    if (chunks <= 1) return 0;
+    return (size_t)WsHeader::kSlotsByteOffset + (size_t)tiles * kVecWordsPerTile * 8u;
 }
 
 rlscan_status rlscan_workspace_init(void* ws, size_t ws_bytes, rlscan_stream_t stream) {
@@ -342,6 +368,36 @@ rlscan_status rlscan_gae_bf16(const uint16_t* rewards, const uint16_t* values,
     GaeCompactArgs a{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
                      advantages, returns, gamma, lambda};
     return launch_gae_compact(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
+}
+
+rlscan_status rlscan_traces_vec(const float* gradients, const float* decay, const float* dones,
+                                const float* seed, float* traces, int64_t num_envs,
+                                int64_t seq_len, int64_t dim, float kappa, void* ws,
+                                size_t ws_bytes, rlscan_stream_t stream) {
+    RLSCAN_TRY(check_shape_vec(num_envs, seq_len, dim));
+    if (std::isnan(kappa)) return set_error(RLSCAN_ERR_BAD_PARAM, "kappa is NaN");
+    if (num_envs == 0 || seq_len == 0 || dim == 0) return RLSCAN_OK;
+    RLSCAN_REQUIRE(gradients, "gradients");
+    RLSCAN_REQUIRE(dones, "dones");
+    RLSCAN_REQUIRE(traces, "traces");
+    const bool vec = dim % 4 == 0 && aligned16(gradients) && aligned16(decay) &&
+                     aligned16(traces) && aligned16(seed);
+    const int G = vec ? 4 : 1;
+    int64_t chunks = 0;
+    const int64_t tiles = traces_vec_tiles(num_envs, seq_len, dim, G, &chunks);
+    if (chunks > 1) {
+        if (!ws)
+            return set_error(RLSCAN_ERR_WORKSPACE,
+                             "this shape needs a workspace (rlscan_traces_vec_workspace_bytes)");
+        if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+            return set_error(RLSCAN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        if (ws_bytes < (size_t)WsHeader::kSlotsByteOffset + (size_t)tiles * kVecWordsPerTile * 8u)
+            return set_error(RLSCAN_ERR_WORKSPACE,
+                             "workspace too small (rlscan_traces_vec_workspace_bytes)");
+    }
+    VecTraceArgs a{gradients, decay, dones, seed, traces, num_envs, seq_len, dim, kappa};
+    return launch_traces_vec(a, G, ws, g_jitter.load(std::memory_order_relaxed),
+                             reinterpret_cast<hipStream_t>(stream));
 }
 
 rlscan_status rlscan_vtrace(const float* log_pi_target, const float* log_pi_behavior,

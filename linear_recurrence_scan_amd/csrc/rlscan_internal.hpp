@@ -72,6 +72,18 @@ rlscan_status set_error(rlscan_status st, const char* msg);
 constexpr int kShortRowTile = 2048;
 constexpr int kShortRowWaves = 4;
 
+// Vector eligibility traces over [E,T,D] (D fastest).
+struct VecTraceArgs {
+    const float *gradients, *decay, *dones, *seed;  // decay [E,T,D] or null; seed [E,D] or null
+    float* traces;
+    int64_t E, T, D;
+    float kappa;  // the decay of every entry when decay is null
+};
+// Tiles of a launch with G columns per lane; *chunks receives the tiles per column block.
+int64_t traces_vec_tiles(int64_t E, int64_t T, int64_t D, int G, int64_t* chunks);
+rlscan_status launch_traces_vec(const VecTraceArgs& a, int G, void* ws, uint32_t jitter,
+                                hipStream_t s);
+
 rlscan_status launch_gae(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_gae_skip(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_gae_compact(const GaeCompactArgs& a, const Plan& plan, void* ws, hipStream_t s);

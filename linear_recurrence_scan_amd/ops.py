@@ -75,6 +75,9 @@ def _declare(L):
     L.rlscan_workspace_init.argtypes = [vp, sz, vp]
     L.rlscan_workspace_error.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     L.rlscan_gae.argtypes = [vp] * 8 + [i64, i64, f32, f32, vp, sz, vp]
+    L.rlscan_traces_vec.argtypes = [vp] * 5 + [i64, i64, i64, f32, vp, sz, vp]
+    L.rlscan_traces_vec_workspace_bytes.argtypes = [i64, i64, i64]
+    L.rlscan_traces_vec_workspace_bytes.restype = sz
     L.rlscan_gae_skip.argtypes = [vp] * 9 + [i64, i64, f32, f32, vp, sz, vp]
     L.rlscan_gae_bf16.argtypes = [vp] * 8 + [i64, i64, f32, f32, vp, sz, vp]
     L.rlscan_vtrace.argtypes = [vp] * 10 + [i64, i64, f32, f32, f32, vp, sz, vp]
@@ -87,7 +90,7 @@ def _declare(L):
     L.rlscan_check_inputs.argtypes = [vp] * 4 + [i64, i64, i64, vp, sz,
                                                  ctypes.POINTER(CheckReport), vp]
     for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
-                 "rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
+                 "rlscan_traces_vec", "rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
                  "rlscan_check_inputs", "rlscan_debug_set_launch_shape",
                  "rlscan_debug_set_lookback_jitter"):
         getattr(L, name).restype = st
@@ -146,16 +149,18 @@ def _shape2(name, t):
     return tuple(t.shape)
 
 
-def workspace(device, num_envs, seq_len):
+def workspace(device, num_envs, seq_len, need=None):
     """Returns (tensor, nbytes) of a zero-initialised look-back workspace cached
     per (device, stream); grows on demand.  Calls on one stream are ordered, so
-    sharing the workspace among them is safe."""
+    sharing the workspace among them is safe.  `need` overrides the byte
+    count rlscan_workspace_bytes gives for [num_envs, seq_len]."""
     device = torch.device(device)
-    need = int(lib().rlscan_workspace_bytes(num_envs, seq_len))
+    if need is None:
+        need = int(lib().rlscan_workspace_bytes(num_envs, seq_len))
     key = (device.index, torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 4096), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(need, 8192), dtype=torch.uint8, device=device)  # >= the header
         _check("rlscan_workspace_init", lib().rlscan_workspace_init(_ptr(ws), ws.numel(), _stream(device)))
         _workspaces[key] = ws
     return ws, ws.numel()
@@ -234,6 +239,15 @@ def rlscan_gae(rewards, values, terminateds, truncateds, bootstrap_values, last_
                           _ptr(bootstrap_values), _ptr(last_value), _ptr(advantages), _ptr(returns),
                           E, T, float(gamma), float(lambda_), _ptr(ws), nws, _stream(dev))
     _check("rlscan_gae", st)
+
+
+def rlscan_traces_vec(gradients, decay, dones, seed_values, traces, kappa):
+    E, T, D = gradients.shape
+    dev = gradients.device
+    ws, nws = workspace(dev, E, T, int(lib().rlscan_traces_vec_workspace_bytes(E, T, D)))
+    st = lib().rlscan_traces_vec(_ptr(gradients), _ptr(decay), _ptr(dones), _ptr(seed_values),
+                                 _ptr(traces), E, T, D, float(kappa), _ptr(ws), nws, _stream(dev))
+    _check("rlscan_traces_vec", st)
 
 
 def rlscan_gae_skip(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
@@ -472,6 +486,24 @@ def _forward(inputs, dones, seed_values, decay, boundary):
 def eligibility_traces(gradients, dones, gamma, lambda_, seed_values=None):
     """Accumulating eligibility traces (forward scan, decay gamma*lambda, ends_at)."""
     return _forward(gradients, dones, seed_values, float(gamma) * float(lambda_), "ends_at")
+
+
+def vector_eligibility_traces(gradients, dones, gamma=1.0, lambda_=1.0, decay=None,
+                              seed_values=None):
+    """Eligibility traces of a vector input [E,T,D] with per-dimension decay:
+    z_t[d] = g_t[d] + b_t[d] (1 - done_{t-1}) z_{t-1}[d], where b = decay
+    ([E,T,D] float32) when given, else gamma * lambda_ for every entry."""
+    if not isinstance(gradients, torch.Tensor) or gradients.dim() != 3:
+        raise ValueError("gradients must be a [num_envs, seq_len, dim] tensor")
+    E, T, D = gradients.shape
+    dev = gradients.device
+    g = _f32("gradients", gradients, (E, T, D))
+    dn = _f32("dones", dones, (E, T), dev)
+    dc = _f32("decay", decay, (E, T, D), dev, optional=True)
+    sv = _f32("seed_values", seed_values, (E, D), dev, optional=True)
+    out = torch.empty_like(g)
+    rlscan_traces_vec(g, dc, dn, sv, out, gamma * lambda_)
+    return out
 
 
 def episodic_prefix_sum(inputs, dones, seed_values=None, boundary="ends_at"):

@@ -180,3 +180,15 @@ def skip_spans(E, T, seed, p_enter=0.02, p_leave=1.0 / 16):
         state = np.where(state, u[:, t] >= p_leave, u[:, t] < p_enter)
         out[:, t] = state
     return out
+
+
+def traces_vec_inputs(E, T, D, seed, p_done=0.01, with_decay=True, seeded=True):
+    """Vector-trace rollout [E,T,D]: gradients ~ N(0,1); per-entry decay
+    ~ U(0.8, 1.0) (per-parameter trace decays near gamma*lambda); dones
+    [E,T] ~ Bern(p_done); seed [E,D] ~ N(0,1)."""
+    rng = _rng(seed)
+    g = rng.standard_normal((E, T, D)).astype(np.float32)
+    decay = rng.uniform(0.8, 1.0, (E, T, D)).astype(np.float32) if with_decay else None
+    dones = (rng.random((E, T)) < p_done).astype(np.float32)
+    seed_v = rng.standard_normal((E, D)).astype(np.float32) if seeded else None
+    return {"gradients": g, "decay": decay, "dones": dones, "seed_values": seed_v}

@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
-    for n in ("rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
+    for n in ("rlscan_traces_vec", "rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
         assert n in names
 
 
@@ -81,6 +81,26 @@ def test_gae_validation(L):
     assert gae(L, lv=P, bv=P) == CONFLICT
     assert gae(L, lv=P, tr=P) == CONFLICT
     assert L.rlscan_gae(P, P, P, N, N, N, P, N, 4, 8, float("nan"), 0.95, N, 0, N) == BAD_PARAM
+
+
+def test_traces_vec_validation(L):
+    def call(g=P, dc=N, dn=P, sd=N, out=P, E=4, T=8, D=16, k=0.9, ws=N, nws=0):
+        return L.rlscan_traces_vec(g, dc, dn, sd, out, E, T, D, k, ws, nws, N)
+    assert call(g=N) == NULL_ARG
+    assert call(dn=N) == NULL_ARG
+    assert call(out=N) == NULL_ARG
+    assert call(E=0) == OK and call(T=0) == OK and call(D=0) == OK
+    assert call(D=-1) == BAD_SHAPE
+    assert call(D=1 << 31) == BAD_SHAPE
+    assert call(E=1 << 20, T=1 << 16, D=1 << 12) == BAD_SHAPE
+    assert call(k=float("nan")) == BAD_PARAM
+    # 64 steps fit one tile: no workspace; 65 need one
+    assert L.rlscan_traces_vec_workspace_bytes(4, 64, 16) == 0
+    need = L.rlscan_traces_vec_workspace_bytes(4, 65, 16)
+    assert need > 4352
+    assert call(T=65) == WORKSPACE
+    assert call(T=65, ws=ctypes.c_void_p(0x100000), nws=need - 8) == WORKSPACE
+    assert call(T=65, ws=ctypes.c_void_p(0x100010), nws=need) == WORKSPACE
 
 
 def test_gae_skip_validation(L):
