@@ -15,9 +15,9 @@
 //   1. every wave loads its S steps and folds them per lane into one affine
 //      map (a, b) per column: z_out = a + b * z_in;
 //   2. the W maps meet in LDS; each wave composes the ones before it;
-//   3. wave 0 finds the value entering the tile: the seed for the first
-//      chunk of t, else a decoupled look-back over the earlier chunks of the
-//      same columns, through 64-bit words that each carry one column's value
+//   3. the last wave finds the value entering the tile: the seed for the
+//      first chunk of t, else a decoupled look-back over the earlier chunks
+//      of the same columns, through 64-bit words that each carry one column's value
 //      and an epoch tag (aggregate 2e+1, inclusive 2e+2), so a word is valid
 //      or not by itself and needs no fence;
 //   4. every wave replays its S steps from its entering value and stores z.
@@ -75,11 +75,23 @@ __device__ __forceinline__ void store_g(float* p, const float (&in)[G]) {
     }
 }
 
-template <int G, int S, int W, bool DECAY>
+// Element `off` past `base`: with OFF32 the offset is a 32-bit byte count
+// added to a wave-uniform base, the scalar-base + vector-offset form of a
+// global access (one VGPR per lane instead of a 64-bit address per access).
+template <bool OFF32>
+__device__ __forceinline__ const float* at(const float* base, int64_t off) {
+    if constexpr (OFF32)
+        return reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) +
+                                              (uint32_t)((uint32_t)off * 4u));
+    return base + off;
+}
+
+template <int G, int S, int W, bool DECAY, bool OFF32>
 __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecGeo g, uint8_t* ws) {
     __shared__ float sh_a[W][G][64];
     __shared__ float sh_b[W][G][64];
     __shared__ float sh_carry[G][64];
+    __shared__ uint32_t sh_found[64];
 
     const int64_t q = blockIdx.x;
     const int64_t k = q / g.col_blocks;
@@ -94,28 +106,46 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
     const int64_t t0 = k * (int64_t)(W * S) + (int64_t)wave * S;
     const bool lookback = g.chunks > 1;
 
+    // The last wave finds the value entering the tile.  It takes the tile's
+    // epoch ticket now, so the atomic's latency hides behind the data loads.
+    const bool finder = wave == W - 1;
     uint64_t ticket = 0;
-    if (lookback && wave == 0 && lane == 0) ticket = epoch_ticket(ws, q);
+    if (lookback && finder && lane == 0) ticket = epoch_ticket(ws, q);
 
-    // 1. loads: gradient, decay and the previous step's done flag per step
-    const int64_t off0 = (e * g.T + t0) * g.D + d0;
+    // 1. loads: gradient, decay and the previous step's done flag per step.
+    // Addresses: the wave's first env at step t0 (uniform; lane 0 is always
+    // active) plus a per-lane offset.
+    const int64_t e_lo = (int64_t)readfirstlane_u64((uint64_t)e);
+    const int64_t ubase = (e_lo * g.T + t0) * g.D;
+    const int64_t rel = active ? (e - e_lo) * g.T * g.D + d0 : 0;
+    const int64_t drel = active ? (e - e_lo) * g.T : 0;
     float gv[S][G], bv[S][G];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int64_t t = t0 + s;
         const bool ok = active && t < g.T;
-        load_g<G>(p.gradients + off0 + s * g.D, ok, gv[s]);
+        load_g<G>(at<OFF32>(p.gradients + ubase + s * g.D, rel), ok, gv[s]);
         float dec[G];
         if constexpr (DECAY) {
-            load_g<G>(p.decay + off0 + s * g.D, ok, dec);
+            load_g<G>(at<OFF32>(p.decay + ubase + s * g.D, rel), ok, dec);
         } else {
 #pragma unroll
             for (int j = 0; j < G; ++j) dec[j] = p.kappa;
         }
-        const float gate = (ok && t > 0) ? 1.f - p.dones[e * g.T + t - 1] : 1.f;
+        const float gate =
+            (ok && t > 0) ? 1.f - *at<OFF32>(p.dones + (e_lo * g.T + t - 1), drel) : 1.f;
 #pragma unroll
         for (int j = 0; j < G; ++j) bv[s][j] = ok ? dec[j] * gate : 1.f;  // identity past T
     }
+
+    // The previous chunk's inclusive words, read behind the data loads: when
+    // that tile has finished, the carry is known without another round trip.
+    uint64_t early[G];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+        early[j] = (lookback && finder && k > 0)
+                       ? slot_load(vec_word<G>(ws, (k - 1) * g.col_blocks + cb, 2, j, lane))
+                       : 0ull;
 
     float A[G], B[G];
 #pragma unroll
@@ -131,6 +161,23 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
             B[j] *= bv[s][j];
         }
 
+    // The finder checks the early words against its epoch and parks the
+    // result in LDS before the barrier.  Consumed only after the barrier, the
+    // loads would be sunk past it by the compiler and their round trip paid
+    // there; an LDS store cannot cross the barrier.
+    const uint32_t epoch = __builtin_amdgcn_readlane((uint32_t)(ticket >> 32), 0);
+    const uint32_t tag_agg = 2u * epoch + 1u, tag_inc = 2u * epoch + 2u;
+    if (finder) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const bool f = lookback && k > 0 && tag_of(early[j]) == tag_inc;
+            bits |= f ? 1u << j : 0u;
+            sh_carry[j][lane] = f ? val_of(early[j]) : 0.f;
+        }
+        sh_found[lane] = bits;
+    }
+
     // 2. wave maps meet in LDS
 #pragma unroll
     for (int j = 0; j < G; ++j) {
@@ -144,6 +191,7 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
         XA[j] = 0.f;
         XB[j] = 1.f;
     }
+#pragma unroll 1
     for (int w = 0; w < wave; ++w)
 #pragma unroll
         for (int j = 0; j < G; ++j) {
@@ -152,22 +200,23 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
             XB[j] *= b;
         }
 
-    // 3. the value entering the tile (wave 0)
-    if (wave == 0) {
-        float TA[G], TB[G];  // the whole tile's map
+    // 3. the value entering the tile (last wave: its own map after the
+    //    others' is the whole tile's map)
+    if (finder) {
+        float TA[G], TB[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) {
-            TA[j] = XA[j];
-            TB[j] = XB[j];
+            TA[j] = fmaf(B[j], XA[j], A[j]);
+            TB[j] = B[j] * XB[j];
         }
-        for (int w = 0; w < W; ++w)
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const float b = sh_b[w][j][lane];
-                TA[j] = fmaf(b, TA[j], sh_a[w][j][lane]);
-                TB[j] *= b;
-            }
         float carry[G];
+        bool found[G];
+        const uint32_t bits = sh_found[lane];
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            found[j] = (bits >> j) & 1u;
+            carry[j] = sh_carry[j][lane];
+        }
         if (k == 0) {
 #pragma unroll
             for (int j = 0; j < G; ++j)
@@ -175,11 +224,7 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
         }
         if (lookback) {
             const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)ticket, 0);
-            const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(ticket >> 32), 0);
-            const uint64_t tk = ((uint64_t)hi << 32) | lo;
-            if (lane == 0) epoch_advance(ws, q, g.num_tiles, tk);
-            const uint32_t epoch = hi;
-            const uint32_t tag_agg = 2u * epoch + 1u, tag_inc = 2u * epoch + 2u;
+            if (lane == 0) epoch_advance(ws, q, g.num_tiles, ((uint64_t)epoch << 32) | lo);
             if (g.jitter) jitter_delay(g.jitter, q);
             if (k == 0) {
 #pragma unroll
@@ -204,15 +249,13 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
                 // inclusive values, so the result is the same bits whichever
                 // inclusive value was found first.
                 int64_t jj[G];
-                bool found[G];
 #pragma unroll
-                for (int j = 0; j < G; ++j) {
-                    jj[j] = k - 1;
-                    found[j] = false;
-                    carry[j] = 0.f;
-                }
+                for (int j = 0; j < G; ++j) jj[j] = k - 1;
                 uint32_t spins = 0;
-                for (;;) {
+                bool all_found = true;
+#pragma unroll
+                for (int j = 0; j < G; ++j) all_found = all_found && found[j];
+                for (bool more = __ballot(!all_found) != 0; more;) {
                     bool all = true;
 #pragma unroll
                     for (int j = 0; j < G; ++j) {
@@ -272,14 +315,24 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
     for (int s = 0; s < S; ++s) {
 #pragma unroll
         for (int j = 0; j < G; ++j) z[j] = fmaf(bv[s][j], z[j], gv[s][j]);
-        if (active && t0 + s < g.T) store_g<G>(p.traces + off0 + s * g.D, z);
+        if (active && t0 + s < g.T)
+            store_g<G>(const_cast<float*>(at<OFF32>(p.traces + ubase + s * g.D, rel)), z);
     }
 }
 
 template <int G, bool DECAY>
 rlscan_status launch_g(const VecTraceArgs& a, const VecGeo& g, void* ws, hipStream_t s) {
-    hipLaunchKernelGGL((traces_vec_kernel<G, kVecS, kVecW, DECAY>), dim3((unsigned)g.num_tiles),
-                       dim3(64 * kVecW), 0, s, a, g, static_cast<uint8_t*>(ws));
+    // a wave's lanes span at most 64*G/D + 1 envs: their offsets from the
+    // wave's first element stay below (64*G + D) * T + D elements
+    const bool off32 = (64 * G + g.D) * g.T + g.D < ((int64_t)1 << 30);
+    if (off32)
+        hipLaunchKernelGGL((traces_vec_kernel<G, kVecS, kVecW, DECAY, true>),
+                           dim3((unsigned)g.num_tiles), dim3(64 * kVecW), 0, s, a, g,
+                           static_cast<uint8_t*>(ws));
+    else
+        hipLaunchKernelGGL((traces_vec_kernel<G, kVecS, kVecW, DECAY, false>),
+                           dim3((unsigned)g.num_tiles), dim3(64 * kVecW), 0, s, a, g,
+                           static_cast<uint8_t*>(ws));
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
     return RLSCAN_OK;
