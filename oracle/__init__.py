@@ -55,6 +55,8 @@ def configure(lib):
     lib.ora_lambda_returns.argtypes = [i64, i64, vp, vp, vp, vp, vp, dbl, dbl, vp]
     lib.ora_discounted_returns.argtypes = [i64, i64, vp, vp, vp, vp, dbl, vp]
     lib.ora_forward_scan.argtypes = [i64, i64, vp, vp, vp, dbl, ctypes.c_int, vp]
+    lib.ora_gae_norm.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, dbl, dbl, dbl, vp, vp, vp]
+    lib.ora_gae_norm.restype = ctypes.c_int
     lib.ora_traces_vec.argtypes = [i64, i64, i64, vp, vp, vp, vp, dbl, vp]
     for name in ("ora_traces_vec", "ora_gae", "ora_gae_skip", "ora_vtrace", "ora_retrace", "ora_lambda_returns",
                  "ora_discounted_returns", "ora_forward_scan"):
@@ -240,3 +242,21 @@ def traces_vec(gradients, dones, kappa=1.0, decay=None, seed_values=None):
                                 _ptr(out))
     _check(rc, "traces_vec")
     return out
+
+
+def gae_norm(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
+             bootstrap_values=None, last_value=None, eps=1e-8):
+    """GAE advantages normalised over the batch, (A - mean) / (std + eps) with
+    the unbiased std; returns (adv_norm, returns, (mean, std)), float64."""
+    E, T = _shape(rewards)
+    r, v, te = _f32(rewards, (E, T)), _f32(values, (E, T)), _f32(terminateds, (E, T))
+    tr, bv = _f32(truncateds, (E, T)), _f32(bootstrap_values, (E, T))
+    lv = _f32(last_value, (E,))
+    adv = np.empty((E, T), np.float64)
+    ret = np.empty((E, T), np.float64)
+    st = np.zeros(2, np.float64)
+    rc = _load().ora_gae_norm(E, T, _ptr(r), _ptr(v), _ptr(te), _ptr(tr), _ptr(bv), _ptr(lv),
+                              float(gamma), float(lambda_), float(eps), _ptr(adv), _ptr(ret),
+                              _ptr(st))
+    _check(rc, "gae_norm")
+    return adv, ret, (float(st[0]), float(st[1]))

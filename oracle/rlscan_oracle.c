@@ -372,3 +372,35 @@ int ora_traces_vec(int64_t E, int64_t T, int64_t D, const float* gradients, cons
     }
     return 0;
 }
+
+/*
+ * GAE with advantage normalisation ([P] Sec. 9.3 plans fused advantage
+ * normalisation).  Reading: the usual batch whitening of PPO advantages,
+ * over all E*T steps,
+ *   mean = sum A / N,   std = sqrt( sum (A - mean)^2 / (N - 1) )   (N >= 2; 0 when N = 1),
+ *   adv_t = (A_t - mean) / (std + eps),
+ * with A the GAE advantages of ora_gae; returns stay A + V (unnormalised).
+ * stats (may be NULL) receives mean and std.
+ */
+int ora_gae_norm(int64_t E, int64_t T, const float* rewards, const float* values,
+                 const float* terminateds, const float* truncateds,
+                 const float* bootstrap_values, const float* last_value, double gamma,
+                 double lambda, double eps, double* adv, double* ret, double* stats) {
+    const int rc = ora_gae(E, T, rewards, values, terminateds, truncateds, bootstrap_values,
+                           last_value, gamma, lambda, adv, ret);
+    if (rc != 0) return rc;
+    const int64_t n = E * T;
+    if (n == 0) return 0;
+    double sum = 0.0;
+    for (int64_t i = 0; i < n; ++i) sum += adv[i];
+    const double mean = sum / (double)n;
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; ++i) ss += (adv[i] - mean) * (adv[i] - mean);
+    const double sd = n > 1 ? sqrt(ss / (double)(n - 1)) : 0.0;
+    for (int64_t i = 0; i < n; ++i) adv[i] = (adv[i] - mean) / (sd + eps);
+    if (stats) {
+        stats[0] = mean;
+        stats[1] = sd;
+    }
+    return 0;
+}

@@ -58,6 +58,12 @@ MUTATIONS = [
      "double z = seed ? (double)seed[e * D + d] : 0.0;", "double z = 0.0;", ["traces_vec"]),
     ("traces_vec_seed_transposed", "ora_traces_vec",
      "(double)seed[e * D + d]", "(double)seed[d * E + e]", ["traces_vec"]),
+    ("norm_biased_std", "ora_gae_norm",
+     "sqrt(ss / (double)(n - 1))", "sqrt(ss / (double)n)", ["gae_norm"]),
+    ("norm_eps_inside_sqrt", "ora_gae_norm",
+     "(adv[i] - mean) / (sd + eps)", "(adv[i] - mean) / sqrt(sd * sd + eps)", ["gae_norm"]),
+    ("norm_mean_not_subtracted", "ora_gae_norm",
+     "adv[i] = (adv[i] - mean) / (sd + eps);", "adv[i] = adv[i] / (sd + eps);", ["gae_norm"]),
     ("forward_layout_transposed", "ora_forward_scan",
      "const int64_t i = IDX(e, t);", "const int64_t i = t * E + e;", ["forward"]),
     ("vtrace_beta_uses_rho", "ora_vtrace",
@@ -107,6 +113,9 @@ def _checks(kind):
         yield lambda: pins.test_traces_vec_match_textbook(0, True, True)
         yield lambda: pins.test_traces_vec_match_textbook(1, False, True)
         yield pins.test_traces_vec_done_resets_every_dimension
+    elif kind == "gae_norm":
+        yield pins.test_gae_norm_worked_example
+        yield lambda: pins.test_gae_norm_is_whitened(0)
     elif kind == "vtrace":
         yield lambda: pins.test_vtrace_matches_episode_textbook(0, (0.8, 1.3), "trunc_2d")
         yield pins.test_vtrace_telescoping_sum

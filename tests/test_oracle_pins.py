@@ -725,3 +725,51 @@ def test_traces_vec_done_resets_every_dimension():
     g2[:, :7] = 0.0                      # earlier inputs must not reach t >= 7
     got2 = oracle.traces_vec(g2, dones, 0.0, decay, np.zeros_like(sv))
     assert np.array_equal(got[0, 7:], got2[0, 7:])
+
+
+# ---------------------------------------------------------------------------
+# GAE with advantage normalisation
+# ---------------------------------------------------------------------------
+
+def test_gae_norm_worked_example():
+    """One env, no flags, gamma = 0: the advantages are r - V = 1, 2, 3; the
+    mean is 2 and the unbiased std 1, so the output is -1, 0, 1."""
+    r = np.array([[1.0, 2.0, 3.0]], np.float32)
+    z = np.zeros_like(r)
+    adv, ret, (m, s) = oracle.gae_norm(r, z, z, gamma=0.0, lambda_=0.5, eps=0.0)
+    assert (m, s) == (2.0, 1.0)
+    assert np.array_equal(adv, [[-1.0, 0.0, 1.0]])
+    assert np.array_equal(ret, [[1.0, 2.0, 3.0]])
+    # eps is added to the std, not to the variance: (std + 1) = 2
+    adv, _, _ = oracle.gae_norm(r, z, z, gamma=0.0, lambda_=0.5, eps=1.0)
+    assert np.array_equal(adv, [[-0.5, 0.0, 0.5]])
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_gae_norm_is_whitened(seed):
+    rng = np.random.default_rng(500 + seed)
+    r, v, term, trunc, boot = rand_rollout(rng, 5, 40)
+    adv, _, (m, s) = oracle.gae_norm(r, v, term, trunc, 0.99, 0.95, boot, eps=0.0)
+    assert abs(adv.mean()) < 1e-12
+    assert abs(adv.std(ddof=1) - 1.0) < 1e-12
+    raw, _ = oracle.gae(r, v, term, trunc, 0.99, 0.95, boot)
+    close(adv * s + m, raw)
+
+
+def test_gae_norm_invariant_to_scaling_rewards_and_values():
+    """GAE is linear in (r, V) and the normalisation divides the scale out:
+    multiplying rewards, values and bootstrap values by 4 (exact in fp32)
+    leaves the normalised advantages unchanged."""
+    rng = np.random.default_rng(9)
+    r, v, term, trunc, boot = rand_rollout(rng, 3, 50)
+    a1, _, _ = oracle.gae_norm(r, v, term, trunc, 0.97, 0.9, boot, eps=0.0)
+    a4, _, (m4, s4) = oracle.gae_norm(r * 4, v * 4, term, trunc, 0.97, 0.9, boot * 4, eps=0.0)
+    close(a1, a4)
+    _, _, (m1, s1) = oracle.gae_norm(r, v, term, trunc, 0.97, 0.9, boot, eps=0.0)
+    close([m4, s4], [4 * m1, 4 * s1])
+
+
+def test_gae_norm_single_step_batch():
+    r = np.array([[2.5]], np.float32)
+    adv, _, (m, s) = oracle.gae_norm(r, np.zeros_like(r), np.zeros_like(r), eps=1e-8)
+    assert (m, s) == (2.5, 0.0) and adv[0, 0] == 0.0
