@@ -166,6 +166,31 @@ rlscan_status rlscan_gae(const float* rewards, const float* values, const float*
                          void* ws, size_t ws_bytes, rlscan_stream_t stream);
 
 /*
+ * GAE with batch advantage normalisation -- paper Sec. 9.3 plans fused
+ * advantage normalisation; the formula is the usual whitening of PPO
+ * advantages, over all E*T steps of the call:
+ *   A = the rlscan_gae advantages,  mean = sum A / N,
+ *   std = sqrt(sum (A - mean)^2 / (N - 1))  (0 when N = 1),
+ *   advantages_t = (A_t - mean) / (std + eps).
+ * returns (or NULL) receives the unnormalised A + V; stats (a DEVICE array of
+ * two doubles, or NULL) receives mean and std.  The statistics are merged in
+ * a fixed order in double precision, so repeated calls give the same bits.
+ * Other arguments, NULL rules and conflicts are those of rlscan_gae.  A
+ * workspace of rlscan_gae_norm_workspace_bytes(E, T) bytes is required at
+ * every shape (zeroed once with rlscan_workspace_init; it serves the other
+ * entry points of the stream too).
+ * Errors  as rlscan_gae; eps < 0 or NaN -> BAD_PARAM; missing, misaligned or
+ *         small workspace -> WORKSPACE.
+ */
+rlscan_status rlscan_gae_norm(const float* rewards, const float* values, const float* terminateds,
+                              const float* truncateds, const float* bootstrap_values,
+                              const float* last_value, float* advantages, float* returns,
+                              double* stats, int64_t num_envs, int64_t seq_len, float gamma,
+                              float lambda, float eps, void* ws, size_t ws_bytes,
+                              rlscan_stream_t stream);
+size_t rlscan_gae_norm_workspace_bytes(int64_t num_envs, int64_t seq_len);
+
+/*
  * Vector eligibility traces with per-dimension decay -- returns/traces page,
  * Eligibility Traces (Definition: z_t = g_t + gamma lambda (1 - d_{t-1})
  * z_{t-1}) for a vector input; per-dimension beta is what paper Sec. 9.2

@@ -24,8 +24,10 @@ struct GaeOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = true;
     static constexpr bool kEdgesAtLoad = (F & kTrunc) == 0;
-    static constexpr bool kFits64 = true;
+    static constexpr bool kStats = (F & kStatsOut) != 0;
+    static constexpr bool kFits64 = !kStats;
     GaeArgs p;
+    __device__ double* stats_out() const { return p.tile_stats; }
     struct Raw {
         float R[G], V[G], TE[G], TR[G], B[G];  // B: full bootstrap array (kBoot2D)
         float SK[G];                           // skip mask (kSkip)

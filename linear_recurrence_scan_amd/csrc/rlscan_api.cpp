@@ -153,6 +153,13 @@ rlscan_status check_shape_vec(int64_t E, int64_t T, int64_t D) {
     return RLSCAN_OK;
 }
 
+// Byte offset of the per-tile statistics of rlscan_gae_norm: past the
+// look-back slots of the smallest tiles any plan uses, 256-byte aligned.
+size_t norm_stats_offset(int64_t E, int64_t T) {
+    const int64_t tiles = (E * T + kMinTile - 1) / kMinTile;
+    return ((size_t)WsHeader::kSlotsByteOffset + (size_t)tiles * 32u + 255u) & ~(size_t)255u;
+}
+
 // Look-back words of one vector-trace tile: 3 per column, 64 lanes of up to 4
 // columns each (sized for 4 whatever the launch uses).
 constexpr size_t kVecWordsPerTile = 3 * 4 * 64;
@@ -213,6 +220,46 @@ size_t rlscan_workspace_bytes(int64_t num_envs, int64_t seq_len) {
     if (check_shape(num_envs, seq_len) != RLSCAN_OK || empty_batch(num_envs, seq_len)) return 0;
     const int64_t N = num_envs * seq_len;
     return ws_bytes_for_tiles((N + kMinTile - 1) / kMinTile);
+}
+
+size_t rlscan_gae_norm_workspace_bytes(int64_t num_envs, int64_t seq_len) {
+    if (check_shape(num_envs, seq_len) != RLSCAN_OK || empty_batch(num_envs, seq_len)) return 0;
+    const int64_t tiles = (num_envs * seq_len + kMinTile - 1) / kMinTile;
+    return norm_stats_offset(num_envs, seq_len) + (size_t)tiles * 32u + 64u;
+}
+
+rlscan_status rlscan_gae_norm(const float* rewards, const float* values, const float* terminateds,
+                              const float* truncateds, const float* bootstrap_values,
+                              const float* last_value, float* advantages, float* returns,
+                              double* stats, int64_t num_envs, int64_t seq_len, float gamma,
+                              float lambda, float eps, void* ws, size_t ws_bytes,
+                              rlscan_stream_t stream) {
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (std::isnan(gamma) || std::isnan(lambda) || !(eps >= 0.f))
+        return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN or eps is negative or NaN");
+    if (empty_batch(num_envs, seq_len)) return RLSCAN_OK;
+    RLSCAN_REQUIRE(rewards, "rewards");
+    RLSCAN_REQUIRE(values, "values");
+    RLSCAN_REQUIRE(terminateds, "terminateds");
+    RLSCAN_REQUIRE(advantages, "advantages");
+    if (last_value && bootstrap_values)
+        return set_error(RLSCAN_ERR_CONFLICT, "pass either last_value or bootstrap_values, not both");
+    if (last_value && truncateds)
+        return set_error(RLSCAN_ERR_CONFLICT, "last_value cannot be combined with truncateds; use bootstrap_values");
+    if (!ws) return set_error(RLSCAN_ERR_WORKSPACE, "normalisation needs a workspace (rlscan_gae_norm_workspace_bytes)");
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+        return set_error(RLSCAN_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < rlscan_gae_norm_workspace_bytes(num_envs, seq_len))
+        return set_error(RLSCAN_ERR_WORKSPACE, "workspace too small (rlscan_gae_norm_workspace_bytes)");
+    const bool vec = aligned16(rewards) && aligned16(values) && aligned16(terminateds) &&
+                     aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(advantages) &&
+                     aligned16(returns);
+    Plan plan;
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    GaeArgs a{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+              advantages, returns, gamma, lambda, nullptr, nullptr};
+    return launch_gae_norm(a, plan, ws, norm_stats_offset(num_envs, seq_len), num_envs * seq_len,
+                           eps, stats, reinterpret_cast<hipStream_t>(stream));
 }
 
 size_t rlscan_traces_vec_workspace_bytes(int64_t num_envs, int64_t seq_len, int64_t dim) {

@@ -17,6 +17,7 @@ struct GaeArgs {
     float *advantages, *returns;
     float gamma, lambda;
     const float* skip;  // observation-skip mask, or null
+    double* tile_stats; // per-tile (count, mean, M2) of the advantages, or null
 };
 
 // Compact rollout format: bf16 values (raw 16-bit storage), one-byte flags.
@@ -86,6 +87,10 @@ rlscan_status launch_traces_vec(const VecTraceArgs& a, int G, void* ws, uint32_t
 
 rlscan_status launch_gae(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_gae_skip(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
+// GAE writing per-tile statistics, then the batch statistics and the
+// normalisation of the advantages in place (op_gae_norm.hip).
+rlscan_status launch_gae_norm(const GaeArgs& a, const Plan& plan, void* ws, size_t stats_off,
+                              int64_t N, float eps, double* stats_out, hipStream_t s);
 rlscan_status launch_gae_compact(const GaeCompactArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_vtrace(const VtraceArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s);

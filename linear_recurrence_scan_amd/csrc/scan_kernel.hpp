@@ -29,6 +29,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "rlscan_internal.hpp"
 #include "scan_core.hpp"
 
@@ -43,6 +45,7 @@ enum : unsigned {
     kLogpBehavior = 8u,  // V-trace log_pi_behavior given
     kSameClip = 16u,     // V-trace rho_bar == c_bar
     kSkip = 32u,         // GAE observation-skip mask given
+    kStatsOut = 64u,     // per-tile statistics of the outputs written (advantage normalisation)
 };
 
 struct SegInfo {
@@ -103,6 +106,33 @@ struct IsStaged {
 struct TileShared {
     float wave_a[8], wave_b[8];
     float carry;
+    float st_n[8], st_m[8], st_m2[8];  // per-wave output statistics (ops that ask for them)
+};
+
+// Count, mean and sum of squared deviations of a set of outputs.  Merging
+// two sets is Chan et al.'s pairwise update:
+//   n = na + nb,  d = mb - ma,  m = ma + d nb / n,  M2 = M2a + M2b + d^2 na nb / n.
+struct Stat {
+    float n, m, m2;
+};
+
+__device__ __forceinline__ Stat stat_merge(Stat a, Stat b) {
+    const float n = a.n + b.n;
+    const float w = n > 0.f ? b.n / n : 0.f;
+    const float d = b.m - a.m;
+    return Stat{n, fmaf(d, w, a.m), a.m2 + b.m2 + d * d * a.n * w};
+}
+
+// Ops that declare `static constexpr bool kStats = true` get the statistics
+// of their scan outputs over each tile written to `op.stats_out()[4*q ...]`
+// as (count, mean, M2) doubles.
+template <class Op, class = void>
+struct WantsStats {
+    static constexpr bool value = false;
+};
+template <class Op>
+struct WantsStats<Op, std::void_t<decltype(Op::kStats)>> {
+    static constexpr bool value = Op::kStats;
 };
 
 template <class Op, int WAVES, int SEGS, bool LOOKBACK, bool FAST>
@@ -243,6 +273,8 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
     }
 
     // phase 3: apply the carries and write the outputs
+    constexpr bool kStats = WantsStats<Op>::value;
+    Stat st{0.f, 0.f, 0.f};
     float xs = fmaf(wexcl.b, x, wexcl.a);  // value entering this wave's first segment
 #pragma unroll
     for (int s = 0; s < SEGS; ++s) {
@@ -259,6 +291,49 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
         }
         op.template epilogue<FAST>(tl, gr, A, prevA, al[s], be[s], kp[s]);
         xs = fmaf(segtot[s].b, xs, segtot[s].a);
+        if constexpr (kStats) {  // this group's valid outputs, merged into the lane's
+            float n = 0.f, sum = 0.f;
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                if (bit(gr.valid, j)) {
+                    n += 1.f;
+                    sum += A[j];
+                }
+            const float m = n > 0.f ? sum / n : 0.f;
+            float m2 = 0.f;
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                if (bit(gr.valid, j)) m2 = fmaf(A[j] - m, A[j] - m, m2);
+            st = stat_merge(st, Stat{n, m, m2});
+        }
+    }
+    if constexpr (kStats) {
+        // lanes: butterfly merges (a fixed pattern, so the result is
+        // reproducible); waves: merged in order by thread 0
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const Stat o{__shfl_xor(st.n, off), __shfl_xor(st.m, off), __shfl_xor(st.m2, off)};
+            st = stat_merge(st, o);
+        }
+        if constexpr (WAVES > 1) {
+            if (lane == 0) {
+                sh.st_n[wave] = st.n;
+                sh.st_m[wave] = st.m;
+                sh.st_m2[wave] = st.m2;
+            }
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                st = Stat{sh.st_n[0], sh.st_m[0], sh.st_m2[0]};
+#pragma unroll
+                for (int u = 1; u < WAVES; ++u) st = stat_merge(st, Stat{sh.st_n[u], sh.st_m[u], sh.st_m2[u]});
+            }
+        }
+        if (threadIdx.x == 0) {
+            double* out = op.stats_out() + 4 * q;
+            out[0] = st.n;
+            out[1] = st.m;
+            out[2] = st.m2;
+        }
     }
 }
 

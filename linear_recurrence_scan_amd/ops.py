@@ -75,6 +75,9 @@ def _declare(L):
     L.rlscan_workspace_init.argtypes = [vp, sz, vp]
     L.rlscan_workspace_error.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     L.rlscan_gae.argtypes = [vp] * 8 + [i64, i64, f32, f32, vp, sz, vp]
+    L.rlscan_gae_norm.argtypes = [vp] * 9 + [i64, i64, f32, f32, f32, vp, sz, vp]
+    L.rlscan_gae_norm_workspace_bytes.argtypes = [i64, i64]
+    L.rlscan_gae_norm_workspace_bytes.restype = sz
     L.rlscan_traces_vec.argtypes = [vp] * 5 + [i64, i64, i64, f32, vp, sz, vp]
     L.rlscan_traces_vec_workspace_bytes.argtypes = [i64, i64, i64]
     L.rlscan_traces_vec_workspace_bytes.restype = sz
@@ -90,7 +93,7 @@ def _declare(L):
     L.rlscan_check_inputs.argtypes = [vp] * 4 + [i64, i64, i64, vp, sz,
                                                  ctypes.POINTER(CheckReport), vp]
     for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
-                 "rlscan_traces_vec", "rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
+                 "rlscan_gae_norm", "rlscan_traces_vec", "rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
                  "rlscan_check_inputs", "rlscan_debug_set_launch_shape",
                  "rlscan_debug_set_lookback_jitter"):
         getattr(L, name).restype = st
@@ -241,6 +244,18 @@ def rlscan_gae(rewards, values, terminateds, truncateds, bootstrap_values, last_
     _check("rlscan_gae", st)
 
 
+def rlscan_gae_norm(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+                    advantages, returns, stats, gamma, lambda_, eps):
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    ws, nws = workspace(dev, E, T, int(lib().rlscan_gae_norm_workspace_bytes(E, T)))
+    st = lib().rlscan_gae_norm(_ptr(rewards), _ptr(values), _ptr(terminateds), _ptr(truncateds),
+                               _ptr(bootstrap_values), _ptr(last_value), _ptr(advantages),
+                               _ptr(returns), _ptr(stats), E, T, float(gamma), float(lambda_),
+                               float(eps), _ptr(ws), nws, _stream(dev))
+    _check("rlscan_gae_norm", st)
+
+
 def rlscan_traces_vec(gradients, decay, dones, seed_values, traces, kappa):
     E, T, D = gradients.shape
     dev = gradients.device
@@ -367,6 +382,27 @@ def gae(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
     else:
         rlscan_gae_skip(r, v, te, tr, bv, lv, sk, adv, ret, gamma, lambda_)
     return (adv, ret) if want_returns else adv
+
+
+def gae_normalized(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
+                   bootstrap_values=None, last_value=None, eps=1e-8, want_returns=False):
+    """GAE advantages whitened over the batch, (A - mean) / (std + eps) with the
+    unbiased std.  Returns (advantages, returns or None, stats) where stats is
+    a float64 tensor [mean, std] on the device."""
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    r = _f32("rewards", rewards, (E, T))
+    v = _f32("values", values, (E, T), dev)
+    te = _f32("terminateds", terminateds, (E, T), dev)
+    tr = _f32("truncateds", truncateds, (E, T), dev, optional=True)
+    bv = _f32("bootstrap_values", bootstrap_values, (E, T), dev, optional=True)
+    lv = _f32("last_value", last_value, (E,), dev, optional=True)
+    _debug_check("gae_normalized", terminateds=te, truncateds=tr, bootstrap_values=bv)
+    adv = torch.empty_like(r)
+    ret = torch.empty_like(r) if want_returns else None
+    stats = torch.zeros(2, dtype=torch.float64, device=dev)
+    rlscan_gae_norm(r, v, te, tr, bv, lv, adv, ret, stats, gamma, lambda_, eps)
+    return adv, ret, stats
 
 
 def gae_bf16(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,

@@ -37,7 +37,7 @@ def declared_functions():
 
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
-    for n in ("rlscan_traces_vec", "rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
+    for n in ("rlscan_gae_norm", "rlscan_traces_vec", "rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix"):
         assert n in names
 
 
@@ -81,6 +81,27 @@ def test_gae_validation(L):
     assert gae(L, lv=P, bv=P) == CONFLICT
     assert gae(L, lv=P, tr=P) == CONFLICT
     assert L.rlscan_gae(P, P, P, N, N, N, P, N, 4, 8, float("nan"), 0.95, N, 0, N) == BAD_PARAM
+
+
+def test_gae_norm_validation(L):
+    need = L.rlscan_gae_norm_workspace_bytes(4, 8)
+    assert need > 4352
+    W = ctypes.c_void_p(0x100000)
+
+    def call(r=P, v=P, te=P, tr=N, bv=N, lv=N, adv=P, ret=N, st=N, E=4, T=8, eps=1e-8, ws=W,
+             nws=need):
+        return L.rlscan_gae_norm(r, v, te, tr, bv, lv, adv, ret, st, E, T, 0.99, 0.95, eps, ws,
+                                 nws, N)
+    for kw in ("r", "v", "te", "adv"):
+        assert call(**{kw: N}) == NULL_ARG, kw
+    assert call(E=0, ws=N, nws=0) == OK
+    assert call(T=-1) == BAD_SHAPE
+    assert call(lv=P, bv=P) == CONFLICT
+    assert call(eps=-1.0) == BAD_PARAM
+    assert call(eps=float("nan")) == BAD_PARAM
+    assert call(ws=N, nws=0) == WORKSPACE            # needed at every shape
+    assert call(nws=need - 8) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(0x100010)) == WORKSPACE
 
 
 def test_traces_vec_validation(L):

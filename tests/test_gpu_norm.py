@@ -1,0 +1,112 @@
+"""GPU parity of GAE with batch advantage normalisation (rlscan_gae_norm)
+against the float64 oracle.
+
+Tolerance.  The fp32 advantages satisfy |dA| <= tol * max(1, |A|) <= tol * M
+with M = max(1, max |A|) (the bound of the fp32 entry points).  The mean
+then moves by at most tol*M and the unbiased std by at most about tol*M, so
+adv = (A - mean) / (std + eps) moves by at most
+    tol * M * (2 + |adv|) / (std + eps),
+plus the fp32 rounding of the final (A - mean) * (1 / (std + eps)), taken as
+1e-6 * (1 + |adv|).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_recurrence_scan_amd import ops, synth
+
+pytestmark = pytest.mark.gpu
+f32 = np.float32
+
+
+def tol_for(T):
+    return 1e-4 if T <= 4096 else 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible AMD GPU"
+    assert ops.lib() is not None
+    yield
+    assert ops.workspace_error() == 0, "a look-back wait exceeded its bound"
+
+
+def dev(x):
+    return None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to("cuda")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy().astype(np.float64)
+
+
+def check(d, T, eps=1e-8, what=""):
+    wa, wr, (wm, ws) = oracle.gae_norm(d["rewards"], d["values"], d["terminateds"], d["truncateds"],
+                                       f32(0.99), f32(0.95), d["bootstrap_values"], d["last_value"],
+                                       eps=float(f32(eps)))
+    adv, ret, st = ops.gae_normalized(dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]),
+                                      dev(d["truncateds"]), 0.99, 0.95, dev(d["bootstrap_values"]),
+                                      dev(d["last_value"]), eps=eps, want_returns=True)
+    raw, _ = oracle.gae(d["rewards"], d["values"], d["terminateds"], d["truncateds"], f32(0.99),
+                        f32(0.95), d["bootstrap_values"], d["last_value"])
+    tol = tol_for(T)
+    M = max(1.0, float(np.abs(raw).max()))
+    g = host(adv)
+    bound = tol * M * (2.0 + np.abs(wa)) / (ws + float(f32(eps))) + 1e-6 * (1.0 + np.abs(wa))
+    ratio = np.abs(g - wa) / bound
+    worst = np.unravel_index(np.argmax(ratio), ratio.shape)
+    assert ratio.max() <= 1.0, (f"{what}: {ratio.max():.3f}x the bound at {worst}: gpu {g[worst]!r} "
+                                f"oracle {wa[worst]!r}")
+    s = host(st)
+    assert abs(s[0] - wm) <= tol * M and abs(s[1] - ws) <= tol * M, (s, wm, ws)
+    rr = host(ret)
+    assert np.max(np.abs(rr - wr) / np.maximum(1.0, np.abs(wr))) <= tol
+    return adv, st
+
+
+SHAPES = [
+    (512, 1024, "2d"),
+    (37, 1000, "2d"),       # look-back across rows
+    (5, 3, "last"),         # rows shorter than four steps
+    (300, 257, None),
+    (3, 4099, "2d"),
+    (1, 20000, "2d"),
+]
+
+
+@pytest.mark.parametrize("E,T,boot", SHAPES)
+def test_gae_norm_parity(E, T, boot):
+    trunc = boot == "2d"
+    d = synth.gae_inputs(E, T, seed=E * 3 + T, p_term=0.02, p_trunc=0.01 if trunc else 0.0,
+                         truncations=trunc, boot=boot)
+    check(d, T, what=f"{E}x{T}")
+
+
+def test_gae_norm_full_size_workload():
+    check(synth.gae_trunc(), 1024, what="4096x1024")
+
+
+def test_gae_norm_large_eps_and_offset_advantages():
+    """Advantages far from zero mean (values biased by -50) and eps = 0.5."""
+    d = synth.gae_inputs(64, 500, seed=5, boot="2d")
+    d["values"] = (d["values"] - 50.0).astype(f32)
+    check(d, 500, eps=0.5, what="offset")
+
+
+def test_gae_norm_single_step():
+    d = synth.gae_inputs(1, 1, seed=1, truncations=False, boot=None)
+    adv, st = check(d, 1, what="1x1")
+    assert host(adv)[0, 0] == 0.0 and host(st)[1] == 0.0
+
+
+def test_gae_norm_is_reproducible():
+    d = synth.gae_trunc(E=300, T=1000, seed=8)
+    args = (dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]), dev(d["truncateds"]),
+            0.99, 0.95, dev(d["bootstrap_values"]))
+    a1, _, s1 = ops.gae_normalized(*args)
+    a2, _, s2 = ops.gae_normalized(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2) and torch.equal(s1, s2)
