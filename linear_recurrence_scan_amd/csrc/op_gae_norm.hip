@@ -31,7 +31,8 @@ __device__ __forceinline__ StatD merge_d(StatD a, StatD b) {
     return StatD{n, a.m + d * w, a.m2 + b.m2 + d * d * a.n * w};
 }
 
-constexpr int kFinalThreads = 256;
+constexpr int kFinalThreads = 1024;
+constexpr int kFinalBatch = 4;  // triples a thread loads before merging them
 
 // result[0] = mean, result[1] = std (unbiased; 0 for one step),
 // result[2] = 1 / (std + eps).
@@ -41,9 +42,20 @@ __global__ __launch_bounds__(kFinalThreads) void stats_finalize_kernel(const dou
                                                                        double* user) {
     __shared__ StatD sh[kFinalThreads];
     const int i = threadIdx.x;
+    // thread i merges tiles i, i + 1024, i + 2048, ... in that order; the
+    // loads of a batch are all issued before the first merge
     StatD acc{0.0, 0.0, 0.0};
-    for (int64_t t = i; t < num_tiles; t += kFinalThreads)
-        acc = merge_d(acc, StatD{tiles[4 * t], tiles[4 * t + 1], tiles[4 * t + 2]});
+    for (int64_t t0 = i; t0 < num_tiles; t0 += (int64_t)kFinalBatch * kFinalThreads) {
+        StatD b[kFinalBatch];
+#pragma unroll
+        for (int u = 0; u < kFinalBatch; ++u) {
+            const int64_t t = t0 + (int64_t)u * kFinalThreads;
+            b[u] = t < num_tiles ? StatD{tiles[4 * t], tiles[4 * t + 1], tiles[4 * t + 2]}
+                                 : StatD{0.0, 0.0, 0.0};
+        }
+#pragma unroll
+        for (int u = 0; u < kFinalBatch; ++u) acc = merge_d(acc, b[u]);
+    }
     sh[i] = acc;
     __syncthreads();
     for (int stride = kFinalThreads / 2; stride >= 1; stride >>= 1) {

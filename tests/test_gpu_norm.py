@@ -102,8 +102,11 @@ def test_gae_norm_single_step():
     assert host(adv)[0, 0] == 0.0 and host(st)[1] == 0.0
 
 
-def test_gae_norm_is_reproducible():
-    d = synth.gae_trunc(E=300, T=1000, seed=8)
+@pytest.mark.parametrize("E,T", [(300, 1000), (512, 1024)])
+def test_gae_norm_is_reproducible(E, T):
+    """Both paths: rows straddling tiles (three launches) and rows of whole
+    tiles (one cooperative launch when the grid fits the device)."""
+    d = synth.gae_trunc(E=E, T=T, seed=8)
     args = (dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]), dev(d["truncateds"]),
             0.99, 0.95, dev(d["bootstrap_values"]))
     a1, _, s1 = ops.gae_normalized(*args)
