@@ -199,3 +199,21 @@ def test_gae_bf16_empty_batch():
     te = torch.empty(0, 16, dtype=torch.uint8, device="cuda")
     adv = ops.gae_bf16(r, r, te)
     assert adv.shape == (0, 16)
+
+
+def test_gae_bf16_signed_zeros_and_exact_values():
+    """Inputs that are exact in bf16 with results exact in fp32 and bf16:
+    gamma = 0.5, lambda = 1, small dyadic rewards, zero and negative-zero
+    values; the outputs must be those exact values."""
+    E, T = 4, 16
+    r = np.tile(np.array([0.25, -0.5, 0.0, 1.0], f32), (E, T // 4))
+    v = np.zeros((E, T), f32)
+    v[:, ::2] = -0.0
+    term = np.zeros((E, T), f32)
+    term[:, 7] = 1.0
+    host_, wide = compact_case({"rewards": r, "values": v, "terminateds": term, "truncateds": None,
+                                "bootstrap_values": None, "last_value": None})
+    want, _ = run_oracle(wide, 0.5, 1.0)
+    adv, _ = run_gpu(host_, 0.5, 1.0)
+    got = adv.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(got, want)

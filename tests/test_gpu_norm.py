@@ -113,3 +113,15 @@ def test_gae_norm_is_reproducible(E, T):
     a2, _, s2 = ops.gae_normalized(*args)
     torch.cuda.synchronize()
     assert torch.equal(a1, a2) and torch.equal(s1, s2)
+
+
+def test_gae_norm_two_steps_and_constant_advantages():
+    """N = 2 (the smallest unbiased std); and a batch whose advantages are all
+    equal (std 0): the output is then 0 everywhere."""
+    d = synth.gae_inputs(1, 2, seed=3, truncations=False, boot=None)
+    check(d, 2, what="1x2")
+    E, T = 8, 64
+    z = np.zeros((E, T), f32)
+    r = np.full((E, T), 0.5, f32)
+    adv, _, st = ops.gae_normalized(dev(r), dev(z), dev(z), None, 0.0, 0.95)
+    assert np.all(host(adv) == 0.0) and host(st)[1] == 0.0

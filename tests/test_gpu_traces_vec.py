@@ -136,3 +136,18 @@ def test_traces_vec_empty():
     g = torch.empty(0, 5, 4, device="cuda")
     out = ops.vector_eligibility_traces(g, torch.empty(0, 5, device="cuda"))
     assert out.shape == (0, 5, 4)
+
+
+@pytest.mark.parametrize("E,T,D", [(1, 1, 1), (1, 1, 4), (3, 2, 5), (1, 65, 1), (2, 130, 3)])
+def test_traces_vec_degenerate_shapes(E, T, D):
+    """One step, one dimension, odd dimensions, chunk boundaries just crossed."""
+    d = synth.traces_vec_inputs(E, T, D, seed=E + 10 * T + 100 * D, p_done=0.1)
+    got, want = run(d)
+    assert_close(got, want, T, f"traces {E}x{T}x{D}")
+
+
+def test_traces_vec_long_chain_many_columns():
+    """131072 steps: 2048 chunks per column block, 64 column blocks."""
+    d = synth.traces_vec_inputs(2, 131072, 32, seed=77, p_done=1e-4, with_decay=True)
+    got, want = run(d)
+    assert_close(got, want, 131072, "traces 2x131072x32")
