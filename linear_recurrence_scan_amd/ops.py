@@ -375,6 +375,8 @@ def gae(rewards, values, terminateds, truncateds=None, gamma=0.99, lambda_=0.95,
     lv = _f32("last_value", last_value, (E,), dev, optional=True)
     sk = _f32("skip_mask", skip_mask, (E, T), dev, optional=True)
     _debug_check("gae", terminateds=te, truncateds=tr, bootstrap_values=bv)
+    if sk is not None:
+        _debug_check("gae (skip_mask as 0/1 flags)", terminateds=sk)
     adv = torch.empty_like(r)
     ret = torch.empty_like(r) if want_returns else None
     if sk is None:
@@ -537,6 +539,7 @@ def vector_eligibility_traces(gradients, dones, gamma=1.0, lambda_=1.0, decay=No
     dn = _f32("dones", dones, (E, T), dev)
     dc = _f32("decay", decay, (E, T, D), dev, optional=True)
     sv = _f32("seed_values", seed_values, (E, D), dev, optional=True)
+    _debug_check("vector_eligibility_traces", terminateds=dn)
     out = torch.empty_like(g)
     rlscan_traces_vec(g, dc, dn, sv, out, gamma * lambda_)
     return out

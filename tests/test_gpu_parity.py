@@ -569,6 +569,21 @@ def test_checks_env_switch_guards_the_helpers(monkeypatch):
     assert_close(got, want, T, "after checks")
 
 
+def test_checks_env_switch_covers_skip_mask_and_trace_dones(monkeypatch):
+    monkeypatch.setenv("RLSCAN_CHECKS", "1")
+    d = synth.gae_inputs(4, 300, seed=2)
+    sk = synth.skip_spans(4, 300, seed=3)
+    sk[1, 5] = 2.0
+    with pytest.raises(ValueError, match="flags_not_binary=1"):
+        ops.gae(dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]), dev(d["truncateds"]),
+                0.99, 0.95, dev(d["bootstrap_values"]), skip_mask=dev(sk))
+    t = synth.traces_vec_inputs(2, 100, 8, seed=4)
+    bad = t["dones"].copy()
+    bad[0, 3] = -1.0
+    with pytest.raises(ValueError, match="flags_not_binary=1"):
+        ops.vector_eligibility_traces(dev(t["gradients"]), dev(bad), 0.9, 0.9)
+
+
 # ---------------------------------------------------------------------------
 # every compiled launch shape (the planner picks only some of them by default)
 # ---------------------------------------------------------------------------
