@@ -62,21 +62,24 @@ struct GaeOp {
                            float (&al)[G], float (&be)[G], Keep (&kp)[G]) const {
         float VN[G];
         scan_prev<G>(w.V, w.halo, VN);
-        const float gl = p.gamma * p.lambda;
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const bool edge = bit(gr.edges, j);
             float b = w.B[j];
             if constexpr ((F & kTrunc) == 0) b = w.eb.at(gr, j);
             // successor value: bootstrap at the row end, else (1-trunc) V_{t+1} + B_t
-            const float vnext = edge ? b : fmaf(1.f - w.TR[j], VN[j], b);
-            const float done = fminf(w.TE[j] + w.TR[j], 1.f);
-            float a = fmaf(p.gamma * (1.f - w.TE[j]), vnext, w.R[j]) - w.V[j];
-            float bb = edge ? 0.f : gl * (1.f - done);  // A_T = 0
+            const float omt = 1.f - w.TR[j];
+            const float vnext = edge ? b : fmaf(omt, VN[j], b);
+            // For 0/1 flags, exactly: gamma (1 - term) = fma(term, -gamma, gamma), and
+            // gamma lambda (1 - min(term + trunc, 1)) = (lambda * gamma (1 - term)) (1 - trunc).
+            const float g1 = fmaf(w.TE[j], -p.gamma, p.gamma);
+            float a = fmaf(g1, vnext, w.R[j]) - w.V[j];
+            const float keep = edge ? 0.f : omt;  // A_T = 0
+            float bb = (p.lambda * g1) * keep;
             if constexpr ((F & kSkip) != 0) {
                 if (w.SK[j] != 0.f) {  // masked: no TD error, carry undiscounted
                     a = 0.f;
-                    bb = edge ? 0.f : 1.f - done;
+                    bb = (1.f - w.TE[j]) * keep;
                 }
             }
             al[j] = bit(gr.valid, j) ? a : 0.f;

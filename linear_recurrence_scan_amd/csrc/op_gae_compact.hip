@@ -52,16 +52,17 @@ struct GaeCompactOp {
                            float (&al)[G], float (&be)[G], Keep (&kp)[G]) const {
         float VN[G];
         scan_prev<G>(w.V, w.halo, VN);
-        const float gl = p.gamma * p.lambda;
 #pragma unroll
         for (int j = 0; j < G; ++j) {
             const bool edge = bit(gr.edges, j);
             float b = w.B[j];
             if constexpr ((F & kTrunc) == 0) b = w.eb.at(gr, j);
-            const float vnext = edge ? b : fmaf(1.f - w.TR[j], VN[j], b);
-            const float done = fminf(w.TE[j] + w.TR[j], 1.f);
-            const float a = fmaf(p.gamma * (1.f - w.TE[j]), vnext, w.R[j]) - w.V[j];
-            const float bb = edge ? 0.f : gl * (1.f - done);  // A_T = 0
+            const float omt = 1.f - w.TR[j];
+            const float vnext = edge ? b : fmaf(omt, VN[j], b);
+            // the fp32 GAE op's coefficients, the same operations (exact for 0/1 flags)
+            const float g1 = fmaf(w.TE[j], -p.gamma, p.gamma);
+            const float a = fmaf(g1, vnext, w.R[j]) - w.V[j];
+            const float bb = (p.lambda * g1) * (edge ? 0.f : omt);  // A_T = 0
             al[j] = bit(gr.valid, j) ? a : 0.f;
             be[j] = bit(gr.valid, j) ? bb : 1.f;
             kp[j].v = w.V[j];
