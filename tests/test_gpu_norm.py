@@ -102,10 +102,34 @@ def test_gae_norm_single_step():
     assert host(adv)[0, 0] == 0.0 and host(st)[1] == 0.0
 
 
-@pytest.mark.parametrize("E,T", [(300, 1000), (512, 1024)])
+def test_gae_norm_many_tiles():
+    """More than 8192 tiles (8200 x 1024): the tile statistics are merged in a
+    launch of their own instead of by every normalising workgroup."""
+    check(synth.gae_trunc(E=8200, T=1024, seed=12), 1024, what="8200x1024")
+
+
+@pytest.mark.parametrize("E,T", [(64, 515), (300, 1000)])
+def test_gae_norm_unaligned_advantages(E, T):
+    """Advantages starting one element into their allocation take the
+    element-wise loads and stores of the normalising pass; the results are
+    those of the aligned call, bit for bit."""
+    d = synth.gae_inputs(E, T, seed=E + T, p_term=0.01, p_trunc=0.005, boot="2d")
+    args = [dev(d[k]) for k in ("rewards", "values", "terminateds", "truncateds",
+                                "bootstrap_values")]
+    want, _, want_st = ops.gae_normalized(*args[:4], 0.99, 0.95, args[4])
+    buf = torch.zeros(E * T + 1, device="cuda")
+    adv = buf[1:].view(E, T)
+    st = torch.zeros(2, dtype=torch.float64, device="cuda")
+    ops.rlscan_gae_norm(*args, None, adv, None, st, 0.99, 0.95, 1e-8)
+    torch.cuda.synchronize()
+    assert torch.equal(adv, want) and torch.equal(st, want_st)
+    assert buf[0].item() == 0.0
+
+
+@pytest.mark.parametrize("E,T", [(300, 1000), (512, 1024), (8200, 1024)])
 def test_gae_norm_is_reproducible(E, T):
-    """Both paths: rows straddling tiles (three launches) and rows of whole
-    tiles (one cooperative launch when the grid fits the device)."""
+    """Rows straddling tiles, rows of whole tiles, and a grid above 8192
+    tiles (separate merge launch): the same bits on every call."""
     d = synth.gae_trunc(E=E, T=T, seed=8)
     args = (dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]), dev(d["truncateds"]),
             0.99, 0.95, dev(d["bootstrap_values"]))
