@@ -79,6 +79,28 @@ rlscan_status finish_plan(int64_t E, int64_t T, int tile, int waves, bool vec_ok
     return RLSCAN_OK;
 }
 
+// Compute units of the current device, 0 when they cannot be read; cached
+// per device.
+int device_cus() {
+    static std::atomic<int> cache[64];  // CU count + 1; 0 = not read yet
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    int v = (dev >= 0 && dev < 64) ? cache[dev].load(std::memory_order_relaxed) : 0;
+    if (v == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            cus = 0;
+        }
+        v = cus + 1;
+        if (dev >= 0 && dev < 64) cache[dev].store(v, std::memory_order_relaxed);
+    }
+    return v - 1;
+}
+
 // Plans a launch of a 4-elements-per-lane kernel.
 rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
     const int64_t N = E * T;
@@ -89,23 +111,43 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
         tile = kShortRowTile;
         waves = kShortRowWaves;
     } else if (!cfg_override(tile, waves)) {
-        // Measured on MI355X.  Tiny problems take small tiles so that more
-        // workgroups share the work.  Rows of 4096 steps or longer take
-        // 4096-element tiles of 8 waves x 2 segments (whole rows per tile, or
-        // fewer look-back hops along a long row: 1024 x 4096 V-trace,
-        // 64 x 131072 returns and prefix sums).  Rows that divide 1024 take
-        // 1024-element tiles of 2 waves x 2 segments, which need no
-        // look-back (4096 x 1024 GAE: 1% faster than 2048-element tiles).
-        // Other rows take 2048-element tiles of 4 waves x 2 segments.
+        // Measured on MI355X (fp32 GAE over 1M-8M steps, rows of 333 to 4096
+        // steps, every launch shape).  `one_round` is the number of steps the
+        // device holds at once: 8 waves on each of 4 SIMDs per CU, 8 steps
+        // per lane.
+        //  - Tiny problems take small tiles so that more workgroups share the
+        //    work.
+        //  - Rows of 4096 steps or longer take 4096-element tiles of 8 waves x
+        //    2 segments (whole rows per tile, or fewer look-back hops along a
+        //    long row).
+        //  - Rows that divide 4096 need no look-back at any tile size.  A grid
+        //    of one round (more than half of one_round, at most one_round)
+        //    takes 4096-element tiles of 8 waves: fewer, larger workgroups
+        //    were 0.3-2% faster at 4096 x 1024.  Otherwise small workgroups
+        //    refill freed slots sooner: 1024-element tiles of 2 waves (rows
+        //    that divide 1024), else 2048-element tiles of 4 waves.
+        //  - Other rows straddle tiles, and each tile looks back to its
+        //    predecessor.  From 5/8 of one_round up, 4096-element tiles of 4
+        //    waves x 4 segments halve the look-backs of 2048-element tiles and
+        //    were 6-10% faster (4194 x 1000: 22.5 against 25.0 us); below it,
+        //    2048-element tiles of 4 waves.
+        const int64_t one_round = (int64_t)device_cus() * 4 * 8 * 512;
+        const bool whole_rows = 4096 % T == 0;
         if (N <= (int64_t)256 * 1024) {
             tile = 256;
             waves = 1;
         } else if (T >= 4096) {
             tile = 4096;
             waves = 8;
+        } else if (whole_rows && 2 * N > one_round && N <= one_round) {
+            tile = 4096;
+            waves = 8;
         } else if (1024 % T == 0) {
             tile = 1024;
             waves = 2;
+        } else if (!whole_rows && one_round > 0 && 8 * N >= 5 * one_round) {
+            tile = 4096;
+            waves = 4;
         } else {
             tile = 2048;
             waves = 4;
