@@ -86,16 +86,19 @@ struct VtraceOp {
             // plus one ulp, against some ten more instructions for expf
             const float ratio = __expf(w.LP[j] - w.LB[j]);
             const float rho = fminf(p.rho_bar, ratio);
-            const float c = fminf(p.c_bar, ratio);
-            const float vnext = edge ? b : fmaf(1.f - w.TR[j], VN[j], b);
-            const float done = fminf(w.TE[j] + w.TR[j], 1.f);
-            const float a = rho * (fmaf(p.gamma * (1.f - w.TE[j]), vnext, w.R[j]) - w.V[j]);
-            const float bb = edge ? 0.f : p.gamma * c * (1.f - done);
+            const float c = kSame ? rho : fminf(p.c_bar, ratio);
+            const float omt = 1.f - w.TR[j];
+            const float vnext = edge ? b : fmaf(omt, VN[j], b);
+            // For 0/1 flags, exactly: gamma (1 - term) = fma(term, -gamma, gamma),
+            // and gamma x (1 - min(term + trunc, 1)) = (x * gamma (1 - term)) (1 - trunc).
+            const float g1 = fmaf(w.TE[j], -p.gamma, p.gamma);
+            const float keep = edge ? 0.f : omt;  // 0 at the row end
+            const float a = rho * (fmaf(g1, vnext, w.R[j]) - w.V[j]);
+            const float bb = (c * g1) * keep;
             al[j] = bit(gr.valid, j) ? a : 0.f;
             be[j] = bit(gr.valid, j) ? bb : 1.f;
             kp[j].v = w.V[j];
-            if constexpr (!kSame)
-                kp[j].k = edge ? 0.f : p.gamma * rho * ((1.f - w.TE[j]) * (1.f - w.TR[j]));
+            if constexpr (!kSame) kp[j].k = (rho * g1) * keep;
         }
     }
 
