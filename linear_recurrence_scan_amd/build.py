@@ -36,6 +36,10 @@ def _common(defines) -> list[str]:
         "-Wall", "-Wno-unused-parameter",
         # packed fp32 VALU forms stay disabled in every HIP translation unit
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # the look-back atomics are issued by one lane; the compiler's
+        # wave-level aggregation of atomics made the ticket's add wait for its
+        # return at tile start, ahead of the tile's data loads
+        "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
         *[f"-D{d}" for d in defines],
     ]
 

@@ -23,6 +23,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 
 // A lane's four consecutive bf16 values (8 bytes), widened, in scan order.
 // FAST: one 8-byte load (the tile is whole and the array 8-byte aligned).
+// Otherwise one unconditional load per element (slot_offset): with a branch
+// per element the widening sits inside the branch, the compiler waits for
+// each load before issuing the next, and the one partial tile of a launch
+// took some 20 us under a full memory system, delaying the whole launch.
 template <bool BACKWARD, bool FAST>
 __device__ __forceinline__ void load_bf16_group(const __bf16* __restrict__ tp, const Grp& gr,
                                                 float (&out)[4]) {
@@ -33,12 +37,12 @@ __device__ __forceinline__ void load_bf16_group(const __bf16* __restrict__ tp, c
         for (int k = 0; k < 4; ++k) out[BACKWARD ? 3 - k : k] = f[k];
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            out[j] = bit(gr.valid, j) ? (float)tp[gr.off + flat_of_slot<4, BACKWARD>(j)] : 0.f;
+        for (int j = 0; j < 4; ++j) out[j] = (float)tile_elem(tp, slot_offset<4, BACKWARD>(gr, j));
     }
 }
 
-// A lane's four consecutive one-byte flags (4 bytes) as 0.0f / 1.0f.
+// A lane's four consecutive one-byte flags (4 bytes) as 0.0f / 1.0f; the
+// per-element path as for bf16.
 template <bool BACKWARD, bool FAST>
 __device__ __forceinline__ void load_u8_group(const uint8_t* __restrict__ tp, const Grp& gr,
                                               float (&out)[4]) {
@@ -48,8 +52,7 @@ __device__ __forceinline__ void load_u8_group(const uint8_t* __restrict__ tp, co
         for (int k = 0; k < 4; ++k) out[BACKWARD ? 3 - k : k] = (float)((v >> (8 * k)) & 0xffu);
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            out[j] = bit(gr.valid, j) ? (float)tp[gr.off + flat_of_slot<4, BACKWARD>(j)] : 0.f;
+        for (int j = 0; j < 4; ++j) out[j] = (float)tile_elem(tp, slot_offset<4, BACKWARD>(gr, j));
     }
 }
 

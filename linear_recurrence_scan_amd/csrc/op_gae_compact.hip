@@ -45,7 +45,12 @@ struct GaeCompactOp {
         } else {
             w.eb.load(g, tl, gr, bf(p.last_value), bf(p.bootstrap_values));
         }
-        w.halo = (lane_id() == 0 && si.halo_valid) ? (float)bf(p.values)[si.halo_flat] : 0.f;
+        // V just past the segment, for lane 0's last step; read unconditionally
+        // (at the tile start when there is none: that step is then the last
+        // of the array, a row end, and does not use it)
+        const int64_t h = si.halo_valid ? si.halo_flat : tl.lo;
+        const float keep = (lane_id() == 0 && si.halo_valid) ? 1.f : 0.f;
+        w.halo = (float)bf(p.values)[h] * keep;
     }
 
     __device__ void coeffs(const Geo& g, const Tile& tl, const Grp& gr, const Raw& w,

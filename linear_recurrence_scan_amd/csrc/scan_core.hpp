@@ -163,6 +163,7 @@ struct Grp {
     uint32_t off;    // offset of the group's lowest flat element from the tile start
     uint32_t edges;  // bit j: slot j is the last step of its row (backward) or the first (forward)
     uint32_t valid;  // bit j: slot j lies inside [0, N)
+    uint32_t last;   // offset of the tile's last element inside [0, N)
 };
 
 template <int G, bool BACKWARD>
@@ -178,6 +179,7 @@ __device__ __forceinline__ Grp make_grp_base(const Tile& tl, uint32_t off) {
     Grp r;
     r.off = off;
     r.edges = 0;
+    r.last = tl.rem - 1u;
     if (FAST) {
         r.valid = (1u << G) - 1u;
     } else {
@@ -253,6 +255,24 @@ __device__ __forceinline__ void store16(float* p, f32x4 v) {
 #else
     *reinterpret_cast<f32x4*>(p) = v;
 #endif
+}
+
+// Offset that slot j of the group reads in an unconditional per-element
+// load: its own element, or the tile's last element inside [0, N) for a slot
+// past N.  Every op maps the slots past N to the identity (alpha 0, beta 1)
+// and stores only slots inside [0, N), so what such a slot reads does not
+// matter, as long as it is finite (every input is, by contract).
+template <int G, bool BACKWARD>
+__device__ __forceinline__ uint32_t slot_offset(const Grp& gr, int j) {
+    return bit(gr.valid, j) ? gr.off + (uint32_t)flat_of_slot<G, BACKWARD>(j) : gr.last;
+}
+
+// Element `off` of the tile's array at `tp`, addressed as the tile pointer
+// (the same for the whole wave) plus a 32-bit byte offset (a tile is at most
+// 16K elements), so the load needs no 64-bit address per element.
+template <class T>
+__device__ __forceinline__ T tile_elem(const T* __restrict__ tp, uint32_t off) {
+    return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(tp) + off * (uint32_t)sizeof(T));
 }
 
 // Loads the group's G floats from `tp` (the array's pointer advanced to the

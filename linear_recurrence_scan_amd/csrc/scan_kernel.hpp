@@ -261,7 +261,13 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
     float x = 0.f;
     if constexpr (LOOKBACK) {
         if (wave == 0) {
-            const uint64_t t = readfirstlane_u64(ticket);
+            // The ticket's add was issued at tile start.  The empty asm keeps
+            // the wait for it here, behind the data loads: without it the
+            // compiler makes the ticket wave-uniform right after the add, and
+            // every tile waited out the atomic before issuing a single load.
+            uint32_t tlo = (uint32_t)ticket, thi = (uint32_t)(ticket >> 32);
+            asm volatile("" : "+v"(tlo), "+v"(thi));
+            const uint64_t t = readfirstlane_u64(((uint64_t)thi << 32) | tlo);
             if (lane == 0) epoch_advance(ws, q, g.num_tiles, t);
             x = lookback(ws, (uint32_t)(t >> 32), q, stride, ttot, need_carry, early, g.jitter);
         }

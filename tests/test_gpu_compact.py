@@ -128,6 +128,19 @@ def test_gae_bf16_full_size_workload():
     assert_close_bf16(ret, want_ret, 1024, "returns")
 
 
+@pytest.mark.parametrize("E,T", [(4194, 1000), (12600, 333)])
+def test_gae_bf16_large_rows_straddling_tiles(E, T):
+    """About 4.2M steps in rows that straddle tiles: the 4096-step look-back
+    launch with a partial last tile, whose element-wise loads issue without
+    waiting on one another."""
+    host, wide = compact_case(synth.gae_trunc(E=E, T=T, seed=E + T))
+    want_adv, want_ret = run_oracle(wide)
+    adv, ret = run_gpu(host)
+    assert (E * T) % 4096 != 0
+    assert_close_bf16(adv, want_adv, T, "advantages")
+    assert_close_bf16(ret, want_ret, T, "returns")
+
+
 def test_gae_bf16_matches_fp32_entry_point_rounded():
     """The compact kernel evaluates the fp32 entry point's arithmetic on the
     widened inputs, so its outputs are that entry point's outputs rounded to

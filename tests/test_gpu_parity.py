@@ -232,6 +232,21 @@ def test_gae_full_size_workload():
     assert_close(ret, want_ret, 1024, "returns")
 
 
+@pytest.mark.parametrize("E,T", [(4194, 1000), (12600, 333)])
+def test_gae_large_rows_straddling_tiles(E, T):
+    """About 4.2M steps in rows that straddle tiles: the planner's 4096-step
+    look-back launch, whose last tile is partial (element-wise loads)."""
+    d = synth.gae_trunc(E=E, T=T, seed=E + T)
+    want_adv, want_ret = oracle.gae(d["rewards"], d["values"], d["terminateds"], d["truncateds"],
+                                    f32(0.99), f32(0.95), d["bootstrap_values"])
+    adv, ret = ops.gae(dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]),
+                       dev(d["truncateds"]), 0.99, 0.95, dev(d["bootstrap_values"]),
+                       want_returns=True)
+    assert (E * T) % 4096 != 0
+    assert_close(adv, want_adv, T, "advantages")
+    assert_close(ret, want_ret, T, "returns")
+
+
 # ---------------------------------------------------------------------------
 # V-trace
 # ---------------------------------------------------------------------------
