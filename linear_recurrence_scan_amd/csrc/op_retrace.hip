@@ -46,7 +46,11 @@ struct RetraceOp {
     struct Raw {
         float mu, q, r, te, tr;
         int64_t act;
-        float c_h, q_h;  // halo: c and q of the scan-previous element (lane 0)
+        // halo, the scan-previous step h (the flat-next one) when there is one:
+        // its action, mu and q, and pi[h, lane] (A <= 64) or pi[h, a_h] (lane 0)
+        bool h_ok;
+        int64_t h_act;
+        float h_mu, h_q, h_pi;
         f32x4 pi4[kSlab], qn4[kSlab];  // 16-byte pieces lane + 64*k of the segment's slab
     };
     struct Keep {
@@ -81,13 +85,25 @@ struct RetraceOp {
         w.te = valid ? p.terminateds[f] : 0.f;
         w.tr = (valid && p.truncateds) ? p.truncateds[f] : 0.f;
         w.act = valid ? clamp_action(p.actions[f]) : 0;
-        w.c_h = 0.f;
-        w.q_h = 0.f;
-        if (lane_id() == 0 && si.halo_valid) {
+        w.h_ok = si.halo_valid;
+        w.h_act = 0;
+        w.h_mu = 1.f;
+        w.h_q = 0.f;
+        w.h_pi = 0.f;
+        if (si.halo_valid) {
             const int64_t h = si.halo_flat;
-            const int64_t a = clamp_action(p.actions[h]);
-            w.c_h = p.lambda * fminf(p.c_bar, p.pi_target[h * p.A + a] / p.mu_taken[h]);
-            w.q_h = p.q_taken[h];
+            w.h_mu = p.mu_taken[h];
+            w.h_q = p.q_taken[h];
+            if (p.A <= kWave) {
+                // every lane reads the action (one broadcast) and lane l reads
+                // pi[h, l]; pi[h, a_h] is picked out once the data are in, so
+                // no load of the segment waits for another (a dependent read
+                // here held the next segment's loads back by a round trip)
+                w.h_act = p.actions[h];
+                if (lane_id() < (int)p.A) w.h_pi = p.pi_target[h * p.A + lane_id()];
+            } else if (lane_id() == 0) {
+                w.h_pi = p.pi_target[h * p.A + clamp_action(p.actions[h])];
+            }
         }
     }
 
@@ -151,8 +167,13 @@ struct RetraceOp {
         const float ratio = pia / w.mu;
         const float c = p.lambda * fminf(p.c_bar, ratio);
         const float rho = fminf(p.rho_bar, ratio);
-        const float c_next = wave_shift_prev(c, w.c_h);
-        const float q_next = wave_shift_prev(w.q, w.q_h);
+        float pi_h = w.h_pi;  // pi[h, a_h] (lane 0 suffices)
+        if (p.A <= kWave)
+            pi_h = __int_as_float(__builtin_amdgcn_readlane(
+                __float_as_int(w.h_pi), (int)clamp_action((int64_t)readfirstlane_u64((uint64_t)w.h_act))));
+        const float c_h = w.h_ok ? p.lambda * fminf(p.c_bar, pi_h / w.h_mu) : 0.f;
+        const float c_next = wave_shift_prev(c, c_h);
+        const float q_next = wave_shift_prev(w.q, w.h_q);
         const float done = fminf(w.te + w.tr, 1.f);
         const bool edge = bit(gr.edges, 0);
         const float a = fmaf(p.gamma * (1.f - w.te), expect, w.r) - w.q;

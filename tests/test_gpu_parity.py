@@ -305,6 +305,8 @@ RETRACE_CASES = [
     (6, 300, 5, 0.02),
     (4, 1030, 33, 0.01),
     (3, 129, 128, 0.01),
+    (5, 700, 64, 0.01),     # A = 64: the halo row of pi read one entry per lane
+    (5, 700, 65, 0.01),     # A = 65: the halo's pi[h, a_h] read by lane 0
     (64, 64, 7, 0.05),
     # above 64K steps: 8-wave tiles with the slabs loaded up front (A <= 32)
     (70, 1000, 18, 0.01),   # rows straddle tiles, ragged last tile
