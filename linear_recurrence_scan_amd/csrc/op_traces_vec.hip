@@ -53,14 +53,17 @@ __device__ __forceinline__ uint64_t* vec_word(uint8_t* ws, int64_t q, int which,
     return slots + (((q * 3 + which) * G + j) * 64 + lane);
 }
 
+// G consecutive floats, loaded unconditionally (the caller passes an address
+// inside the array and masks the value arithmetically: a conditional load
+// whose value merges with a default makes the compiler wait for it before the
+// next step's loads issue).
 template <int G>
-__device__ __forceinline__ void load_g(const float* p, bool ok, float (&out)[G]) {
+__device__ __forceinline__ void load_g(const float* p, float (&out)[G]) {
     if constexpr (G == 4) {
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (ok) v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
         out[0] = v.x; out[1] = v.y; out[2] = v.z; out[3] = v.w;
     } else {
-        out[0] = ok ? __builtin_nontemporal_load(p) : 0.f;
+        out[0] = __builtin_nontemporal_load(p);
     }
 }
 
@@ -119,23 +122,33 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
     const int64_t ubase = (e_lo * g.T + t0) * g.D;
     const int64_t rel = active ? (e - e_lo) * g.T * g.D + d0 : 0;
     const int64_t drel = active ? (e - e_lo) * g.T : 0;
+    // Every load is unconditional: a step past T reads step T-1 of the same
+    // row (an inactive lane reads the wave's first column), and the masks are
+    // applied by arithmetic, exactly for finite inputs: g * 0 = 0,
+    // fma(x, 0, 1) = 1, 1 - done * 0 = 1.  So every load of the wave is in
+    // flight at once.
     float gv[S][G], bv[S][G];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int64_t t = t0 + s;
-        const bool ok = active && t < g.T;
-        load_g<G>(at<OFF32>(p.gradients + ubase + s * g.D, rel), ok, gv[s]);
-        float dec[G];
+        const int64_t tc = t < g.T ? t : g.T - 1;  // the step the addresses use
+        const float okf = (active && t < g.T) ? 1.f : 0.f;
+        const float gatef = (active && t < g.T && t > 0) ? 1.f : 0.f;
+        float gr[G], dec[G];
+        load_g<G>(at<OFF32>(p.gradients + ubase + (tc - t0) * g.D, rel), gr);
         if constexpr (DECAY) {
-            load_g<G>(at<OFF32>(p.decay + ubase + s * g.D, rel), ok, dec);
+            load_g<G>(at<OFF32>(p.decay + ubase + (tc - t0) * g.D, rel), dec);
         } else {
 #pragma unroll
             for (int j = 0; j < G; ++j) dec[j] = p.kappa;
         }
-        const float gate =
-            (ok && t > 0) ? 1.f - *at<OFF32>(p.dones + (e_lo * g.T + t - 1), drel) : 1.f;
+        const float dn = *at<OFF32>(p.dones + (e_lo * g.T + (tc > 0 ? tc - 1 : 0)), drel);
+        const float gate = 1.f - dn * gatef;
 #pragma unroll
-        for (int j = 0; j < G; ++j) bv[s][j] = ok ? dec[j] * gate : 1.f;  // identity past T
+        for (int j = 0; j < G; ++j) {
+            gv[s][j] = gr[j] * okf;
+            bv[s][j] = fmaf(dec[j] * gate, okf, 1.f - okf);  // identity past T
+        }
     }
 
     // The previous chunk's inclusive words, read behind the data loads: when
