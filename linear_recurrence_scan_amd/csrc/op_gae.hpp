@@ -51,11 +51,15 @@ struct GaeOp {
             load_group<G, true, FAST>(p.truncateds + tl.lo, gr, w.TR);
             if constexpr ((F & kBoot2D) != 0)
                 load_group<G, true, FAST>(p.bootstrap_values + tl.lo, gr, w.B);
-        } else {
-            w.eb.load(g, tl, gr, p.last_value, p.bootstrap_values);
         }
         if constexpr ((F & kSkip) != 0) load_group<G, true, FAST>(p.skip + tl.lo, gr, w.SK);
         w.halo = (lane_id() == 0 && si.halo_valid) ? p.values[si.halo_flat] : 0.f;
+    }
+
+    // Without truncations: the continuation value of a row end in the group.
+    template <bool FAST>
+    __device__ void load_edges(const Geo& g, const Tile& tl, const Grp& gr, Raw& w) const {
+        if constexpr ((F & kTrunc) == 0) w.eb.load(g, tl, gr, p.last_value, p.bootstrap_values);
     }
 
     __device__ void coeffs(const Geo& g, const Tile& tl, const Grp& gr, const Raw& w,

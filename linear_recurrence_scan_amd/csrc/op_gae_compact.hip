@@ -42,8 +42,6 @@ struct GaeCompactOp {
             load_u8_group<true, FAST>(p.truncateds + tl.lo, gr, w.TR);
             if constexpr ((F & kBoot2D) != 0)
                 load_bf16_group<true, FAST>(bf(p.bootstrap_values) + tl.lo, gr, w.B);
-        } else {
-            w.eb.load(g, tl, gr, bf(p.last_value), bf(p.bootstrap_values));
         }
         // V just past the segment, for lane 0's last step; read unconditionally
         // (at the tile start when there is none: that step is then the last
@@ -51,6 +49,12 @@ struct GaeCompactOp {
         const int64_t h = si.halo_valid ? si.halo_flat : tl.lo;
         const float keep = (lane_id() == 0 && si.halo_valid) ? 1.f : 0.f;
         w.halo = (float)bf(p.values)[h] * keep;
+    }
+
+    // Without truncations: the continuation value of a row end in the group.
+    template <bool FAST>
+    __device__ void load_edges(const Geo& g, const Tile& tl, const Grp& gr, Raw& w) const {
+        if constexpr ((F & kTrunc) == 0) w.eb.load(g, tl, gr, bf(p.last_value), bf(p.bootstrap_values));
     }
 
     __device__ void coeffs(const Geo& g, const Tile& tl, const Grp& gr, const Raw& w,

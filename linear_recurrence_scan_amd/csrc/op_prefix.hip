@@ -27,6 +27,12 @@ struct PrefixOp {
                          Raw& w) const {
         load_group<G, false, FAST>(p.inputs + tl.lo, gr, w.X);
         load_group<G, false, FAST>(p.dones + tl.lo, gr, w.D);
+        w.halo = (!p.starts_at && lane_id() == 0 && si.halo_valid) ? p.dones[si.halo_flat] : 0.f;
+    }
+
+    // The seed of each row that starts in the group.
+    template <bool FAST>
+    __device__ void load_edges(const Geo& g, const Tile& tl, const Grp& gr, Raw& w) const {
 #pragma unroll
         for (int j = 0; j < G; ++j) w.S[j] = 0.f;
         if (p.seed && (gr.edges & gr.valid)) {
@@ -34,7 +40,6 @@ struct PrefixOp {
             for (int j = 0; j < G; ++j)
                 if (bit(gr.edges & gr.valid, j)) w.S[j] = p.seed[row_at(g, tl, gr.off + j)];
         }
-        w.halo = (!p.starts_at && lane_id() == 0 && si.halo_valid) ? p.dones[si.halo_flat] : 0.f;
     }
 
     __device__ void coeffs(const Geo&, const Tile&, const Grp& gr, const Raw& w, float (&al)[G],

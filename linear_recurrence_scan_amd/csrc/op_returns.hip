@@ -36,11 +36,16 @@ struct ReturnsOp {
             load_group<G, true, FAST>(p.truncateds + tl.lo, gr, w.TR);
             if constexpr ((F & kBoot2D) != 0)
                 load_group<G, true, FAST>(p.bootstrap_values + tl.lo, gr, w.B);
-        } else {
-            w.eb.load(g, tl, gr, static_cast<const float*>(nullptr), p.bootstrap_values);
         }
         if constexpr ((F & kNextValues) != 0)
             load_group<G, true, FAST>(p.next_values + tl.lo, gr, w.NV);
+    }
+
+    // Without truncations: bootstrap_values[:, T-1] at a row end in the group.
+    template <bool FAST>
+    __device__ void load_edges(const Geo& g, const Tile& tl, const Grp& gr, Raw& w) const {
+        if constexpr ((F & kTrunc) == 0)
+            w.eb.load(g, tl, gr, static_cast<const float*>(nullptr), p.bootstrap_values);
     }
 
     __device__ void coeffs(const Geo& g, const Tile& tl, const Grp& gr, const Raw& w,

@@ -1,7 +1,8 @@
 // scan_kernel.hpp -- the one templated kernel every estimator runs, and its
 // launcher.  Each estimator (op_*.hip) supplies an Op with
 //   G, BACKWARD                 elements per lane and scan direction
-//   kEdgesAtLoad                load() reads row-end values (needs the mask)
+//   kEdgesAtLoad                the op reads row-end values, in
+//                               load_edges<FAST>(...) (needs the mask)
 //   Raw, Keep                   raw inputs of one lane's G elements, and what
 //                               the epilogue needs besides the scan result
 //   lds_floats_per_wave()       dynamic LDS per wave (0 unless staged)
@@ -178,15 +179,19 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
     // workgroups starve the epilogues of older ones, which then hold their
     // slots longer, so it stays off there.
     if (g.boost) __builtin_amdgcn_s_setprio(3);
-    // Ops that read row-end values during the load phase need the row-end
-    // mask there; for the others it is computed after every load is issued.
+    // The row-end mask costs a few dozen instructions per group, so ops that
+    // read row-end values compute it, and issue those reads (load_edges),
+    // only after the segment's data loads are issued.
     Raw raw[SEGS];
     uint32_t edges[SEGS];
 #pragma unroll
     for (int s = 0; s < SEGS; ++s) {
         Grp gr = lane_grp_base(s);
-        if constexpr (Op::kEdgesAtLoad) gr.edges = edges[s] = lane_edges(s);
         op.template load<FAST>(g, tl, seg_info(s), gr, raw[s]);
+        if constexpr (Op::kEdgesAtLoad) {
+            gr.edges = edges[s] = lane_edges(s);
+            op.template load_edges<FAST>(g, tl, gr, raw[s]);
+        }
         // A pause of about 256 cycles between one segment's loads and the
         // next's.  Measured on MI355X (4096 x 1024 GAE, one round of 8192
         // waves): the loads of both segments issued back to back took 22.2 us
