@@ -31,7 +31,7 @@ template <bool BACKWARD, bool FAST>
 __device__ __forceinline__ void load_bf16_group(const __bf16* __restrict__ tp, const Grp& gr,
                                                 float (&out)[4]) {
     if constexpr (FAST) {
-        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(tp + gr.off));
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(&tile_elem(tp, gr.off)));
         const float f[4] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y)};
 #pragma unroll
         for (int k = 0; k < 4; ++k) out[BACKWARD ? 3 - k : k] = f[k];
@@ -47,7 +47,7 @@ template <bool BACKWARD, bool FAST>
 __device__ __forceinline__ void load_u8_group(const uint8_t* __restrict__ tp, const Grp& gr,
                                               float (&out)[4]) {
     if constexpr (FAST) {
-        const uint32_t v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tp + gr.off));
+        const uint32_t v = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(&tile_elem(tp, gr.off)));
 #pragma unroll
         for (int k = 0; k < 4; ++k) out[BACKWARD ? 3 - k : k] = (float)((v >> (8 * k)) & 0xffu);
     } else {
@@ -63,7 +63,7 @@ __device__ __forceinline__ void store_bf16_group(__bf16* __restrict__ tp, const 
         u32x2 v;
         v.x = pack_bf16(in[BACKWARD ? 3 : 0], in[BACKWARD ? 2 : 1]);
         v.y = pack_bf16(in[BACKWARD ? 1 : 2], in[BACKWARD ? 0 : 3]);
-        *reinterpret_cast<u32x2*>(tp + gr.off) = v;
+        *reinterpret_cast<u32x2*>(const_cast<__bf16*>(&tile_elem<__bf16>(tp, gr.off))) = v;
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)

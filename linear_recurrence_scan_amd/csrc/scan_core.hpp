@@ -269,9 +269,10 @@ __device__ __forceinline__ uint32_t slot_offset(const Grp& gr, int j) {
 
 // Element `off` of the tile's array at `tp`, addressed as the tile pointer
 // (the same for the whole wave) plus a 32-bit byte offset (a tile is at most
-// 16K elements), so the load needs no 64-bit address per element.
+// 16K elements), so the access takes the scalar-base form with one 32-bit
+// offset register instead of a 64-bit address per access.
 template <class T>
-__device__ __forceinline__ T tile_elem(const T* __restrict__ tp, uint32_t off) {
+__device__ __forceinline__ const T& tile_elem(const T* __restrict__ tp, uint32_t off) {
     return *reinterpret_cast<const T*>(reinterpret_cast<const char*>(tp) + off * (uint32_t)sizeof(T));
 }
 
@@ -284,7 +285,7 @@ template <int G, bool BACKWARD, bool FAST>
 __device__ __forceinline__ void load_group(const float* __restrict__ tp, const Grp& gr,
                                            float (&out)[G]) {
     if constexpr (FAST && G == 4) {
-        const f32x4 v = load16(tp + gr.off);
+        const f32x4 v = load16(&tile_elem(tp, gr.off));
         const float f[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) out[BACKWARD ? 3 - k : k] = f[k];
@@ -304,7 +305,7 @@ __device__ __forceinline__ void store_group(float* __restrict__ tp, const Grp& g
         v.y = in[BACKWARD ? 2 : 1];
         v.z = in[BACKWARD ? 1 : 2];
         v.w = in[BACKWARD ? 0 : 3];
-        store16(tp + gr.off, v);
+        store16(const_cast<float*>(&tile_elem(tp, gr.off)), v);
     } else {
 #pragma unroll
         for (int j = 0; j < G; ++j)
