@@ -27,10 +27,14 @@ struct StatD {
     double n, m, m2;
 };
 
-constexpr int kStatThreads = 1024;  // threads of every kernel that merges the triples
-constexpr int kStatWaves = kStatThreads / 64;
-constexpr int kStatBatch = 4;       // triples a thread loads before adding them
+constexpr int kStatBatch = 4;  // triples a thread loads before adding them
+// Grid sizes that take the statistics inside the normalising pass, by the
+// workgroup size that pass uses: 256 threads up to 2048 tiles (each thread
+// adds at most eight triples), 1024 threads up to 8192 tiles.  Larger grids
+// merge the triples in a launch of their own.
+constexpr int64_t kFusedSmallMaxTiles = 2048;
 constexpr int64_t kFusedMaxTiles = 8192;
+constexpr int kFinalThreads = 1024;
 
 // Tile t's triple, or the empty triple past the last tile.  The load itself
 // is unconditional (of tile 0 when t is out of range; num_tiles >= 1) and the
@@ -44,12 +48,13 @@ __device__ __forceinline__ StatD load_triple(const double* tiles, int64_t t, int
     return StatD{tiles[4 * u] * keep, tiles[4 * u + 1] * keep, tiles[4 * u + 2] * keep};
 }
 
-// Thread i's first batch: tiles i, i + 1024, i + 2048, i + 3072.
+// Thread i's first batch: tiles i, i + THREADS, i + 2 THREADS, i + 3 THREADS.
+template <int THREADS>
 __device__ __forceinline__ void load_first_batch(const double* tiles, int64_t num_tiles,
                                                  StatD (&b)[kStatBatch]) {
 #pragma unroll
     for (int u = 0; u < kStatBatch; ++u)
-        b[u] = load_triple(tiles, threadIdx.x + (int64_t)u * kStatThreads, num_tiles);
+        b[u] = load_triple(tiles, threadIdx.x + (int64_t)u * THREADS, num_tiles);
 }
 
 // x from the lane that the DPP control CTRL names, both 32-bit halves moved
@@ -82,11 +87,11 @@ __device__ __forceinline__ double wave_sum(double x) {
     return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
 }
 
-// Workgroup totals of x[0..K) over its kStatThreads threads; every thread
-// gets them.  The wave sums (wave_sum) are added in wave order: the same
-// bits on every call.
-template <int K>
-__device__ __forceinline__ void block_sum(double (&x)[K], double (&sh)[K][kStatWaves]) {
+// Workgroup totals of x[0..K) over its THREADS threads; every thread gets
+// them.  The wave sums (wave_sum) are added in wave order: the same bits on
+// every call.
+template <int THREADS, int K>
+__device__ __forceinline__ void block_sum(double (&x)[K], double (&sh)[K][THREADS / 64]) {
 #pragma unroll
     for (int k = 0; k < K; ++k) x[k] = wave_sum(x[k]);
     const int w = threadIdx.x >> 6;
@@ -98,7 +103,7 @@ __device__ __forceinline__ void block_sum(double (&x)[K], double (&sh)[K][kStatW
     for (int k = 0; k < K; ++k) {
         x[k] = 0.0;
 #pragma unroll
-        for (int v = 0; v < kStatWaves; ++v) x[k] += sh[k][v];
+        for (int v = 0; v < THREADS / 64; ++v) x[k] += sh[k][v];
     }
     __syncthreads();
 }
@@ -114,10 +119,11 @@ struct BatchStats {
 // division is needed per tile.  Thread i takes tiles i, i + 1024, ... in
 // turn, its first batch already loaded into `first`; later batches are read
 // again for the second sum.
+template <int THREADS>
 __device__ BatchStats batch_stats(const double* tiles, int64_t num_tiles,
                                   const StatD (&first)[kStatBatch],
-                                  double (&sh)[2][kStatWaves]) {
-    const int64_t step = (int64_t)kStatBatch * kStatThreads;
+                                  double (&sh)[2][THREADS / 64]) {
+    const int64_t step = (int64_t)kStatBatch * THREADS;
     double ns[2] = {0.0, 0.0};  // count, sum of n m
 #pragma unroll
     for (int u = 0; u < kStatBatch; ++u) {
@@ -127,14 +133,14 @@ __device__ BatchStats batch_stats(const double* tiles, int64_t num_tiles,
     for (int64_t t0 = threadIdx.x + step; t0 < num_tiles; t0 += step) {
         StatD b[kStatBatch];
 #pragma unroll
-        for (int u = 0; u < kStatBatch; ++u) b[u] = load_triple(tiles, t0 + u * kStatThreads, num_tiles);
+        for (int u = 0; u < kStatBatch; ++u) b[u] = load_triple(tiles, t0 + u * THREADS, num_tiles);
 #pragma unroll
         for (int u = 0; u < kStatBatch; ++u) {
             ns[0] += b[u].n;
             ns[1] = fma(b[u].n, b[u].m, ns[1]);
         }
     }
-    block_sum<2>(ns, sh);
+    block_sum<THREADS, 2>(ns, sh);
     const double mean = ns[1] / ns[0];
     double q[1] = {0.0};
 #pragma unroll
@@ -145,28 +151,28 @@ __device__ BatchStats batch_stats(const double* tiles, int64_t num_tiles,
     for (int64_t t0 = threadIdx.x + step; t0 < num_tiles; t0 += step) {
         StatD b[kStatBatch];
 #pragma unroll
-        for (int u = 0; u < kStatBatch; ++u) b[u] = load_triple(tiles, t0 + u * kStatThreads, num_tiles);
+        for (int u = 0; u < kStatBatch; ++u) b[u] = load_triple(tiles, t0 + u * THREADS, num_tiles);
 #pragma unroll
         for (int u = 0; u < kStatBatch; ++u) {
             const double d = b[u].m - mean;
             q[0] += fma(b[u].n * d, d, b[u].m2);
         }
     }
-    double (&sh1)[1][kStatWaves] = *reinterpret_cast<double (*)[1][kStatWaves]>(&sh[0][0]);
-    block_sum<1>(q, sh1);
+    double (&sh1)[1][THREADS / 64] = *reinterpret_cast<double (*)[1][THREADS / 64]>(&sh[0][0]);
+    block_sum<THREADS, 1>(q, sh1);
     return BatchStats{mean, ns[0] > 1.0 ? sqrt(q[0] / (ns[0] - 1.0)) : 0.0};
 }
 
-// One workgroup of kStatThreads threads.  result[0] = mean, result[1] = std,
+// One workgroup of kFinalThreads threads.  result[0] = mean, result[1] = std,
 // result[2] = 1 / (std + eps).
-__global__ __launch_bounds__(kStatThreads) void stats_finalize_kernel(const double* tiles,
+__global__ __launch_bounds__(kFinalThreads) void stats_finalize_kernel(const double* tiles,
                                                                       int64_t num_tiles,
                                                                       double eps, double* result,
                                                                       double* user) {
-    __shared__ double sh[2][kStatWaves];
+    __shared__ double sh[2][kFinalThreads / 64];
     StatD first[kStatBatch];
-    load_first_batch(tiles, num_tiles, first);
-    const BatchStats st = batch_stats(tiles, num_tiles, first, sh);
+    load_first_batch<kFinalThreads>(tiles, num_tiles, first);
+    const BatchStats st = batch_stats<kFinalThreads>(tiles, num_tiles, first, sh);
     if (threadIdx.x == 0) {
         result[0] = st.mean;
         result[1] = st.sd;
@@ -179,21 +185,19 @@ __global__ __launch_bounds__(kStatThreads) void stats_finalize_kernel(const doub
 }
 
 // ---- one launch: statistics merged by every workgroup, then normalisation ----
-constexpr int kNormThreads = kStatThreads;
 constexpr int kNormVecs = 4;  // groups of four advantages per thread and chunk
-constexpr int64_t kNormChunk = (int64_t)kNormThreads * kNormVecs * 4;
-constexpr int kNormMaxBlocks = 256;
+constexpr int64_t kNormMaxThreadsTotal = 256 * 1024;  // workgroups x threads at most
 
 // A thread's sixteen advantages of one chunk: group k is the four consecutive
-// steps at base + 4 (k * kNormThreads + thread) when VEC (16-byte accesses),
-// else element k * kNormThreads + thread for k < 16.
-template <bool VEC>
+// steps at base + 4 (k * THREADS + thread) when VEC (16-byte accesses), else
+// element k * THREADS + thread for k < 16.
+template <int THREADS, bool VEC>
 struct NormChunk {
     float v[kNormVecs * 4];
 
     __device__ __forceinline__ int64_t index(int64_t base, int k, int c) const {
-        return VEC ? base + ((int64_t)k * kNormThreads + threadIdx.x) * 4 + c
-                   : base + (int64_t)(4 * k + c) * kNormThreads + threadIdx.x;
+        return VEC ? base + ((int64_t)k * THREADS + threadIdx.x) * 4 + c
+                   : base + (int64_t)(4 * k + c) * THREADS + threadIdx.x;
     }
 
     __device__ __forceinline__ void load(const float* adv, int64_t base, int64_t n) {
@@ -243,23 +247,24 @@ struct NormChunk {
 // (batch_stats: the same bits in every workgroup).  The loads of its first
 // chunk of advantages are issued right after the first batch of triples, so
 // their latency overlaps the two sums.
-template <bool VEC>
-__global__ __launch_bounds__(kNormThreads) void normalize_fused_kernel(
+template <int THREADS, bool VEC>
+__global__ __launch_bounds__(THREADS) void normalize_fused_kernel(
     float* adv, int64_t n, const double* tiles, int64_t num_tiles, double eps, double* user) {
-    __shared__ double sh[2][kStatWaves];
+    constexpr int64_t kChunk = (int64_t)THREADS * kNormVecs * 4;
+    __shared__ double sh[2][THREADS / 64];
     StatD first[kStatBatch];
-    load_first_batch(tiles, num_tiles, first);
-    int64_t base = (int64_t)blockIdx.x * kNormChunk;
-    NormChunk<VEC> c;
+    load_first_batch<THREADS>(tiles, num_tiles, first);
+    int64_t base = (int64_t)blockIdx.x * kChunk;
+    NormChunk<THREADS, VEC> c;
     c.load(adv, base, n);
-    const BatchStats st = batch_stats(tiles, num_tiles, first, sh);
+    const BatchStats st = batch_stats<THREADS>(tiles, num_tiles, first, sh);
     if (user && blockIdx.x == 0 && threadIdx.x == 0) {
         user[0] = st.mean;
         user[1] = st.sd;
     }
     const float mean = (float)st.mean;
     const float inv = (float)(1.0 / (st.sd + eps));
-    const int64_t stride = (int64_t)gridDim.x * kNormChunk;
+    const int64_t stride = (int64_t)gridDim.x * kChunk;
     for (;;) {
         c.store(adv, base, n, mean, inv);
         base += stride;
@@ -296,6 +301,20 @@ rlscan_status last_launch_status() {
     return err == hipSuccess ? RLSCAN_OK : set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
 }
 
+template <int THREADS>
+rlscan_status launch_fused(float* adv, int64_t N, const double* tiles, int64_t num_tiles, float eps,
+                           double* stats_out, bool aligned, hipStream_t s) {
+    constexpr int64_t chunk = (int64_t)THREADS * kNormVecs * 4;
+    const int64_t blocks = std::min<int64_t>((N + chunk - 1) / chunk, kNormMaxThreadsTotal / THREADS);
+    if (aligned)
+        hipLaunchKernelGGL((normalize_fused_kernel<THREADS, true>), dim3((unsigned)blocks),
+                           dim3(THREADS), 0, s, adv, N, tiles, num_tiles, (double)eps, stats_out);
+    else
+        hipLaunchKernelGGL((normalize_fused_kernel<THREADS, false>), dim3((unsigned)blocks),
+                           dim3(THREADS), 0, s, adv, N, tiles, num_tiles, (double)eps, stats_out);
+    return last_launch_status();
+}
+
 }  // namespace
 
 rlscan_status launch_gae_norm(const GaeArgs& args, const Plan& plan, void* ws, size_t stats_off,
@@ -313,19 +332,11 @@ rlscan_status launch_gae_norm(const GaeArgs& args, const Plan& plan, void* ws, s
         st = launch_gae_op<kStatsOut | kTrunc | kBoot2D>(a, plan, ws, s);
     if (st != RLSCAN_OK) return st;
     const bool aligned = (reinterpret_cast<uintptr_t>(a.advantages) & 15u) == 0;
-    if (plan.geo.num_tiles <= kFusedMaxTiles) {
-        const int64_t blocks = std::min<int64_t>((N + kNormChunk - 1) / kNormChunk, kNormMaxBlocks);
-        if (aligned)
-            hipLaunchKernelGGL(normalize_fused_kernel<true>, dim3((unsigned)blocks),
-                               dim3(kNormThreads), 0, s, a.advantages, N, tiles,
-                               plan.geo.num_tiles, (double)eps, stats_out);
-        else
-            hipLaunchKernelGGL(normalize_fused_kernel<false>, dim3((unsigned)blocks),
-                               dim3(kNormThreads), 0, s, a.advantages, N, tiles,
-                               plan.geo.num_tiles, (double)eps, stats_out);
-        return last_launch_status();
-    }
-    hipLaunchKernelGGL(stats_finalize_kernel, dim3(1), dim3(kStatThreads), 0, s, tiles,
+    if (plan.geo.num_tiles <= kFusedSmallMaxTiles)
+        return launch_fused<256>(a.advantages, N, tiles, plan.geo.num_tiles, eps, stats_out, aligned, s);
+    if (plan.geo.num_tiles <= kFusedMaxTiles)
+        return launch_fused<1024>(a.advantages, N, tiles, plan.geo.num_tiles, eps, stats_out, aligned, s);
+    hipLaunchKernelGGL(stats_finalize_kernel, dim3(1), dim3(kFinalThreads), 0, s, tiles,
                        plan.geo.num_tiles, (double)eps, result, stats_out);
     if ((st = last_launch_status()) != RLSCAN_OK) return st;
     const int64_t blocks = std::min<int64_t>((N + 1023) / 1024, (int64_t)1 << 20);

@@ -108,6 +108,12 @@ def test_gae_norm_many_tiles():
     check(synth.gae_trunc(E=8200, T=1024, seed=12), 1024, what="8200x1024")
 
 
+def test_gae_norm_mid_tiles():
+    """Between 2048 and 8192 tiles (6000 x 1024 in 1024-step tiles): the
+    normalising pass with 1024-thread workgroups."""
+    check(synth.gae_trunc(E=6000, T=1024, seed=13), 1024, what="6000x1024")
+
+
 @pytest.mark.parametrize("E,T", [(64, 515), (300, 1000)])
 def test_gae_norm_unaligned_advantages(E, T):
     """Advantages starting one element into their allocation take the
@@ -126,10 +132,11 @@ def test_gae_norm_unaligned_advantages(E, T):
     assert buf[0].item() == 0.0
 
 
-@pytest.mark.parametrize("E,T", [(300, 1000), (512, 1024), (8200, 1024)])
+@pytest.mark.parametrize("E,T", [(300, 1000), (512, 1024), (6000, 1024), (8200, 1024)])
 def test_gae_norm_is_reproducible(E, T):
-    """Rows straddling tiles, rows of whole tiles, and a grid above 8192
-    tiles (separate merge launch): the same bits on every call."""
+    """Rows straddling tiles, rows of whole tiles, and grids that take the
+    1024-thread normalising pass and the separate merge launch: the same bits
+    on every call."""
     d = synth.gae_trunc(E=E, T=T, seed=8)
     args = (dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]), dev(d["truncateds"]),
             0.99, 0.95, dev(d["bootstrap_values"]))
