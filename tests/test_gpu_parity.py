@@ -429,6 +429,82 @@ def test_prefix_sum_full_size_workload():
     assert_close(got, want, 131072, "prefix")
 
 
+def test_prefix_sum_past_2_31_elements():
+    """More than 2^31 elements in one call (2 rows of 2^30 + 5 steps): 64-bit
+    tile offsets and row arithmetic.  Inputs are drawn on the device from a
+    seeded generator; outputs next to element 2^31, next to the row boundary,
+    at both ends and at random positions are each checked against the oracle
+    run on the episode that ends there (ends_at: the sum of x since the last
+    done)."""
+    E, T = 2, (1 << 30) + 5
+    N = E * T
+    free, _ = torch.cuda.mem_get_info()
+    if free < (40 << 30):
+        pytest.skip("needs about 27 GB of free device memory")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2031)
+    x = torch.rand(E, T, device="cuda", generator=gen)
+    dones = (torch.rand(E, T, device="cuda", generator=gen) < 1e-4).float()
+    out = ops.episodic_prefix_sum(x, dones)
+    torch.cuda.synchronize()
+    picks = [0, 5, (1 << 31) - 3, 1 << 31, (1 << 31) + 2, T - 1, T, T + 1, N - 1]
+    picks += [int(v) for v in np.random.default_rng(7).integers(0, N, 8)]
+    for i in picks:
+        r, t = divmod(i, T)
+        lo = max(0, t - 400_000)
+        nz = torch.nonzero(dones[r, lo:t]).flatten()
+        assert nz.numel() > 0 or lo == 0, "no episode end within 400K steps"
+        s = lo + int(nz[-1]) + 1 if nz.numel() else 0
+        xs = x[r, s:t + 1].cpu().numpy()[None]
+        ds = dones[r, s:t + 1].cpu().numpy()[None]
+        want = oracle.episodic_prefix_sum(xs, ds, None, "ends_at")[0, -1]
+        got = float(out[r, t])
+        assert abs(got - want) <= tol_for(T) * max(1.0, abs(want)), (i, got, want)
+    del x, dones, out
+    torch.cuda.empty_cache()
+
+
+def test_gae_past_2_31_elements():
+    """GAE with truncations over more than 2^31 elements (2 rows of 2^30 + 5
+    steps), the backward tile order: each sampled advantage is checked
+    against the oracle run on the steps from it to the end of its episode (a
+    terminated or truncated step, or the row end), where the window's row-end
+    bootstrap reproduces the recurrence exactly."""
+    E, T = 2, (1 << 30) + 5
+    N = E * T
+    free, _ = torch.cuda.mem_get_info()
+    if free < (90 << 30):
+        pytest.skip("needs about 70 GB of free device memory")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2032)
+    r = torch.randn(E, T, device="cuda", generator=gen)
+    v = torch.randn(E, T, device="cuda", generator=gen)
+    u = torch.rand(E, T, device="cuda", generator=gen)
+    term = (u < 0.005).float()
+    trunc = ((u >= 0.005) & (u < 0.007)).float()
+    del u
+    b = torch.randn(E, T, device="cuda", generator=gen)
+    b[:, :-1] *= trunc[:, :-1]
+    adv = ops.gae(r, v, term, trunc, 0.99, 0.95, b)
+    torch.cuda.synchronize()
+    done = torch.maximum(term, trunc)
+    picks = [0, 5, (1 << 31) - 3, 1 << 31, (1 << 31) + 2, T - 2, T - 1, T, N - 1]
+    picks += [int(x) for x in np.random.default_rng(8).integers(0, N, 8)]
+    for i in picks:
+        row, t = divmod(i, T)
+        hi = min(T, t + 400_000)
+        nz = torch.nonzero(done[row, t:hi]).flatten()
+        assert nz.numel() > 0 or hi == T, "no episode end within 400K steps"
+        e = t + int(nz[0]) if nz.numel() else T - 1
+        w = {k: a[row, t:e + 1].cpu().numpy()[None] for k, a in
+             (("r", r), ("v", v), ("te", term), ("tr", trunc), ("b", b))}
+        want, _ = oracle.gae(w["r"], w["v"], w["te"], w["tr"], f32(0.99), f32(0.95), w["b"])
+        got = float(adv[row, t])
+        assert abs(got - want[0, 0]) <= tol_for(T) * max(1.0, abs(want[0, 0])), (i, got, want[0, 0])
+    del r, v, term, trunc, b, adv, done
+    torch.cuda.empty_cache()
+
+
 def test_prefix_sum_of_ones_is_bit_exact():
     """Counting steps in an episode is exact integer work in fp32 (< 2^24)."""
     E, T = 16, 131072
