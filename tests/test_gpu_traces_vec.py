@@ -146,6 +146,17 @@ def test_traces_vec_degenerate_shapes(E, T, D):
     assert_close(got, want, T, f"traces {E}x{T}x{D}")
 
 
+def test_traces_vec_64bit_offsets():
+    """A shape whose per-wave offsets do not fit the 32-bit offset form,
+    (64*4 + D) * T + D >= 2^30 (2 x (2^22 + 7) x 4): the kernel addresses with
+    64-bit offsets.  Every element is checked."""
+    E, T, D = 2, (1 << 22) + 7, 4
+    assert (64 * 4 + D) * T + D >= 1 << 30
+    d = synth.traces_vec_inputs(E, T, D, seed=78, p_done=0.01, with_decay=True)
+    got, want = run(d)
+    assert_close(got, want, T, f"traces {E}x{T}x{D}")
+
+
 def test_traces_vec_long_chain_many_columns():
     """131072 steps: 2048 chunks per column block, 64 column blocks."""
     d = synth.traces_vec_inputs(2, 131072, 32, seed=77, p_done=1e-4, with_decay=True)
