@@ -244,12 +244,18 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
                 for (int j = 0; j < G; ++j)
                     slot_store(vec_word<G>(ws, q, 2, j, lane), tag_inc, fmaf(TB[j], carry[j], TA[j]));
             } else {
-                // a column whose map ignores its input publishes its
-                // inclusive value at once, the others their aggregate
+                // A column whose map ignores its input, or whose carry the
+                // early read already found, publishes its inclusive value at
+                // once (the same value it would publish after a walk); the
+                // others publish their aggregate first.
+                bool agg[G];
 #pragma unroll
                 for (int j = 0; j < G; ++j) {
+                    agg[j] = TB[j] != 0.f && !found[j];
                     if (TB[j] == 0.f) {
                         slot_store(vec_word<G>(ws, q, 2, j, lane), tag_inc, TA[j]);
+                    } else if (found[j]) {
+                        slot_store(vec_word<G>(ws, q, 2, j, lane), tag_inc, fmaf(TB[j], carry[j], TA[j]));
                     } else {
                         slot_store(vec_word<G>(ws, q, 0, j, lane), tag_agg, TA[j]);
                         slot_store(vec_word<G>(ws, q, 1, j, lane), tag_agg, TB[j]);
@@ -311,7 +317,7 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
                     }
 #pragma unroll
                 for (int j = 0; j < G; ++j)
-                    if (TB[j] != 0.f)
+                    if (agg[j])
                         slot_store(vec_word<G>(ws, q, 2, j, lane), tag_inc, fmaf(TB[j], carry[j], TA[j]));
             }
         }
