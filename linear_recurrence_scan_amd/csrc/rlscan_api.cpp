@@ -111,7 +111,7 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
         tile = kShortRowTile;
         waves = kShortRowWaves;
     } else if (!cfg_override(tile, waves)) {
-        // Measured on MI355X (fp32 GAE over 1M-8M steps, rows of 333 to 4096
+        // Measured on MI355X (fp32 GAE over 1M-67M steps, rows of 333 to 4096
         // steps, every launch shape).  `one_round` is the number of steps the
         // device holds at once: 8 waves on each of 4 SIMDs per CU, 8 steps
         // per lane.
@@ -126,6 +126,10 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
         //    were 0.3-2% faster at 4096 x 1024.  Otherwise small workgroups
         //    refill freed slots sooner: 1024-element tiles of 2 waves (rows
         //    that divide 1024), else 2048-element tiles of 4 waves.
+        //    Past four rounds the larger tiles win again: 4096-element tiles
+        //    of 8 waves took 168-169 us at 32768 x 1024 against 175.5 for
+        //    1024-element ones, and 338 against 343-345 us at 65536 x 1024
+        //    (between two and four rounds the shapes were within noise).
         //  - Other rows straddle tiles, and each tile looks back to its
         //    predecessor.  From 5/8 of one_round up, 4096-element tiles of 4
         //    waves x 4 segments halve the look-backs of 2048-element tiles and
@@ -139,7 +143,8 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
         } else if (T >= 4096) {
             tile = 4096;
             waves = 8;
-        } else if (whole_rows && 2 * N > one_round && N <= one_round) {
+        } else if (whole_rows && one_round > 0 &&
+                   ((2 * N > one_round && N <= one_round) || N > 4 * one_round)) {
             tile = 4096;
             waves = 8;
         } else if (1024 % T == 0) {

@@ -163,6 +163,21 @@ def test_gae_parity(E, T, boot):
     assert_close(ret, want_ret, T, "returns")
 
 
+def test_gae_whole_rows_past_four_rounds():
+    """17000 x 1024 (17.4M steps): rows that divide the tile, more than four
+    rounds of resident workgroups on a 256-CU device, the planner's large-grid
+    branch (4096-step tiles of 8 waves)."""
+    E, T = 17000, 1024
+    d = synth.gae_inputs(E, T, seed=17000, p_term=0.005, p_trunc=0.002, truncations=True, boot="2d")
+    want_adv, want_ret = oracle.gae(d["rewards"], d["values"], d["terminateds"], d["truncateds"],
+                                    f32(0.99), f32(0.95), d["bootstrap_values"], d["last_value"])
+    adv, ret = ops.gae(dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]),
+                       dev(d["truncateds"]), 0.99, 0.95, dev(d["bootstrap_values"]),
+                       dev(d["last_value"]), want_returns=True)
+    assert_close(adv, want_adv, T, "advantages")
+    assert_close(ret, want_ret, T, "returns")
+
+
 def test_gae_without_truncations_reads_only_last_bootstrap_column():
     E, T = 64, 777
     d = synth.gae_inputs(E, T, seed=3, truncations=False, boot=None)
