@@ -411,6 +411,18 @@ def test_discounted_full_size_workload():
     assert_close(got, want, 131072, "discounted")
 
 
+def test_lambda_returns_at_the_long_row_size():
+    """TD(lambda) over 64 x 131072 (the long-row workload's shape, with next
+    values and the long-row flag rates): the same look-back kernel family as
+    discounted returns with its extra input stream."""
+    d = synth.returns_inputs(64, 131072, seed=64131072, p_term=1e-4, p_trunc=5e-5)
+    want = oracle.lambda_returns(d["rewards"], d["next_values"], d["terminateds"], d["truncateds"],
+                                 f32(0.999), f32(0.95), d["bootstrap_values"])
+    got = ops.lambda_returns(dev(d["rewards"]), dev(d["next_values"]), dev(d["terminateds"]),
+                             dev(d["truncateds"]), 0.999, 0.95, dev(d["bootstrap_values"]))
+    assert_close(got, want, 131072, "lambda returns 64x131072")
+
+
 # ---------------------------------------------------------------------------
 # forward scans
 # ---------------------------------------------------------------------------
