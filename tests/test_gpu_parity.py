@@ -146,6 +146,7 @@ GAE_SHAPES = [
     (2, 8191, "last"),
     (1, 20000, "2d"),
     (300, 257, "2d"),
+    (2, 1 << 20, "2d"),      # 256-tile look-back chains, every element checked
 ]
 
 
@@ -427,7 +428,7 @@ def test_lambda_returns_at_the_long_row_size():
 # forward scans
 # ---------------------------------------------------------------------------
 
-PREFIX_CASES = [(8, 131072), (50, 1000), (3, 4097), (100, 17), (7, 1), (2, 10000)]
+PREFIX_CASES = [(8, 131072), (50, 1000), (3, 4097), (100, 17), (7, 1), (2, 10000), (2, 1 << 20)]
 
 
 @pytest.mark.parametrize("E,T", PREFIX_CASES)
