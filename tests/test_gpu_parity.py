@@ -273,6 +273,7 @@ VTRACE_CASES = [
     (7, 999, True, 0.01, "trunc_last", (0.8, 1.2)),
     (40, 100, False, 0.0, None, (2.0, 0.5)),
     (2, 9000, False, 0.0, "last", (1.0, 1.0)),
+    (2, 1 << 20, True, 0.002, "2d", (1.0, 1.0)),   # 256-tile look-back chains
     # rows shorter than a lane's four-element group (kernels of their own)
     (5, 2, False, 0.0, "last", (1.0, 1.0)),
     (6, 3, True, 0.0, "last", (0.8, 1.2)),
@@ -382,7 +383,7 @@ def test_retrace_full_size_workload():
 # TD(lambda) and discounted returns
 # ---------------------------------------------------------------------------
 
-RETURNS_CASES = [(8, 131072), (33, 1000), (4, 5000), (100, 64), (3, 3), (1, 70001)]
+RETURNS_CASES = [(8, 131072), (33, 1000), (4, 5000), (100, 64), (3, 3), (1, 70001), (2, 1 << 20)]
 
 
 @pytest.mark.parametrize("E,T", RETURNS_CASES)
