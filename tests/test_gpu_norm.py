@@ -114,6 +114,14 @@ def test_gae_norm_mid_tiles():
     check(synth.gae_trunc(E=6000, T=1024, seed=13), 1024, what="6000x1024")
 
 
+@pytest.mark.parametrize("E,T", [(17000, 1024), (32768, 1024)])
+def test_gae_norm_past_four_rounds(E, T):
+    """Grids past four rounds of resident workgroups take 4096-step tiles:
+    4250 tiles, and exactly 8192 (the most the 1024-thread normalising pass
+    takes with every workgroup merging the statistics itself)."""
+    check(synth.gae_trunc(E=E, T=T, seed=E), T, what=f"{E}x{T}")
+
+
 @pytest.mark.parametrize("E,T", [(64, 515), (300, 1000)])
 def test_gae_norm_unaligned_advantages(E, T):
     """Advantages starting one element into their allocation take the
