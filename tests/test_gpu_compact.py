@@ -128,6 +128,16 @@ def test_gae_bf16_full_size_workload():
     assert_close_bf16(ret, want_ret, 1024, "returns")
 
 
+def test_gae_bf16_past_four_rounds():
+    """17000 x 1024: rows that divide the tile, more than four rounds of
+    resident workgroups (4096-step tiles of 8 waves), every element."""
+    host, wide = compact_case(synth.gae_trunc(E=17000, T=1024, seed=17000))
+    want_adv, want_ret = run_oracle(wide)
+    adv, ret = run_gpu(host)
+    assert_close_bf16(adv, want_adv, 1024, "advantages")
+    assert_close_bf16(ret, want_ret, 1024, "returns")
+
+
 @pytest.mark.parametrize("E,T", [(4194, 1000), (12600, 333)])
 def test_gae_bf16_large_rows_straddling_tiles(E, T):
     """About 4.2M steps in rows that straddle tiles: the 4096-step look-back

@@ -88,6 +88,16 @@ def test_gae_skip_full_size_workload():
     assert_close(ret, wr, 1024, "returns")
 
 
+def test_gae_skip_past_four_rounds():
+    """17000 x 1024 with a span mask: more than four rounds of resident
+    workgroups (4096-step tiles of 8 waves)."""
+    d = synth.gae_trunc(E=17000, T=1024, seed=17001)
+    d["skip"] = synth.skip_spans(17000, 1024, seed=17002)
+    (adv, ret), (wa, wr) = run(d)
+    assert_close(adv, wa, 1024, "advantages")
+    assert_close(ret, wr, 1024, "returns")
+
+
 def test_gae_skip_all_zero_mask_equals_gae_bitwise():
     d = synth.gae_trunc(E=256, T=1000, seed=4)
     args = [dev(d[k]) for k in ("rewards", "values", "terminateds", "truncateds")]
