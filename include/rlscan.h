@@ -83,9 +83,14 @@ const char* rlscan_status_string(rlscan_status status);
  * ("" if none).  Valid until the next rlscan call on the same thread. */
 const char* rlscan_last_error(void);
 
-/* Bytes of workspace that suffice for any entry point at this shape (the
- * Retrace entry point uses the same bound).  Returns 0 for an empty batch or
- * an invalid shape. */
+/* Bytes of workspace that suffice for rlscan_gae, rlscan_gae_skip,
+ * rlscan_gae_bf16, rlscan_vtrace, rlscan_retrace, rlscan_returns and
+ * rlscan_prefix at this shape.  Returns 0 when no call at this shape takes a
+ * look-back, i.e. when every row fits one tile: at most 256 steps in all, or
+ * seq_len a power of two no larger than 256 (every tile then holds whole
+ * rows); those calls then accept ws = NULL.  Also 0 for an empty batch or an
+ * invalid shape.  (rlscan_check_inputs always needs a workspace of at least
+ * the 4352-byte header.) */
 size_t rlscan_workspace_bytes(int64_t num_envs, int64_t seq_len);
 
 /* Zero-fill a workspace (enqueued on `stream`, with a fill kernel so the call
@@ -94,8 +99,10 @@ size_t rlscan_workspace_bytes(int64_t num_envs, int64_t seq_len);
 rlscan_status rlscan_workspace_init(void* ws, size_t ws_bytes, rlscan_stream_t stream);
 
 /* Reads back the workspace's error word (synchronous: waits for `stream`).
- * Non-zero means a look-back wait exceeded its bound and the affected
- * outputs are invalid; the word is sticky until rlscan_workspace_init. */
+ * Non-zero means a look-back wait exceeded its bound (about a second): the
+ * tile that gave up took a NaN carry, so the affected outputs are NaN rather
+ * than plausible wrong values.  The word is sticky until
+ * rlscan_workspace_init. */
 rlscan_status rlscan_workspace_error(const void* ws, uint32_t* error_out, rlscan_stream_t stream);
 
 /*
@@ -118,7 +125,7 @@ rlscan_status rlscan_workspace_error(const void* ws, uint32_t* error_out, rlscan
  * Pass a forward scan's dones as `terminateds`.
  * The call is SYNCHRONOUS (it waits for `stream`) and must not be captured
  * in a graph.  It keeps its counters in 32 bytes of the header of a
- * workspace (256-byte aligned, at least rlscan_workspace_bytes(1, 1) bytes)
+ * workspace (256-byte aligned, at least 4352 bytes)
  * and clears them itself; the look-back state in that workspace is left as
  * it was, so the workspace of the estimator calls can be passed.
  * Returns RLSCAN_OK when every count is zero and RLSCAN_ERR_DATA otherwise
@@ -298,7 +305,12 @@ rlscan_status rlscan_vtrace(const float* log_pi_target, const float* log_pi_beha
  *         and its outputs are then meaningless); truncateds [E,T] or NULL
  *         (no truncations).  mu_taken must be > 0.
  * Outputs q_ret [E,T]; advantages [E,T] or NULL to skip.
- * Errors  NULL_ARG; BAD_SHAPE for E, T < 0 or A outside [1, 128].
+ * Any number of actions A >= 1 is accepted (the API Reference places no
+ * bound on num_actions); up to 128 actions a segment's slab of pi and
+ * next_q_all is staged whole in on-chip memory, above that each step's row
+ * is reduced across the wavefront.
+ * Errors  NULL_ARG; BAD_SHAPE for E, T < 0, A < 1 or A >= 2^31, or
+ *         E*T*A > 2^46.
  */
 rlscan_status rlscan_retrace(const float* pi_target, const float* mu_taken, const float* q_taken,
                              const float* next_q_all, const int64_t* actions,

@@ -41,6 +41,17 @@ rlscan_status rlscan_debug_set_launch_shape(int tile, int waves);
  * while no other thread is calling the library.  Always returns RLSCAN_OK. */
 rlscan_status rlscan_debug_set_lookback_jitter(uint32_t seed);
 
+/* Bound of every look-back wait, in polls, for every later call in the
+ * process; 0 restores the default (about a second of waiting).  A wait that
+ * reaches the bound gives up: the tile takes a NaN carry, so its outputs and
+ * every output of the row that depends on them become NaN, and the sticky
+ * error word of the workspace is set (rlscan_workspace_error).  A small bound
+ * together with rlscan_debug_set_lookback_jitter makes that happen on
+ * purpose, so a test can check that a give-up is never silent; every kernel
+ * still exits normally.  Process-wide; set it while no other thread is
+ * calling the library.  Always returns RLSCAN_OK. */
+rlscan_status rlscan_debug_set_spin_limit(uint32_t polls);
+
 #ifdef __cplusplus
 }
 #endif

@@ -43,6 +43,7 @@ struct VecGeo {
     int64_t chunks;      // ceil(T / (W*S))
     int64_t num_tiles;   // chunks * col_blocks
     uint32_t jitter;
+    uint32_t spins;  // polls a look-back wait makes before it gives up
 };
 
 // Word (which: 0 = aggregate a, 1 = aggregate b, 2 = inclusive) of column
@@ -293,14 +294,13 @@ __global__ __launch_bounds__(64 * W) void traces_vec_kernel(VecTraceArgs p, VecG
                         }
                     }
                     if (__ballot(!all) == 0) break;
-                    if (++spins > kSpinLimit) {
-                        if (lane == 0)
-                            __hip_atomic_fetch_or(reinterpret_cast<uint32_t*>(ws) + WsHeader::kError, 1u,
-                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (++spins > g.spins) {
+                        // give up: a NaN carry marks every value derived from it
+                        if (lane == 0) flag_timeout(ws);
 #pragma unroll
                         for (int j = 0; j < G; ++j)
                             if (!found[j]) {
-                                carry[j] = 0.f;
+                                carry[j] = timeout_carry();
                                 jj[j] = k - 1;
                             }
                         break;
@@ -369,7 +369,7 @@ int64_t traces_vec_tiles(int64_t E, int64_t T, int64_t D, int G, int64_t* chunks
 }
 
 rlscan_status launch_traces_vec(const VecTraceArgs& a, int G, void* ws, uint32_t jitter,
-                                hipStream_t s) {
+                                uint32_t spins, hipStream_t s) {
     VecGeo g;
     g.E = a.E;
     g.T = a.T;
@@ -378,6 +378,7 @@ rlscan_status launch_traces_vec(const VecTraceArgs& a, int G, void* ws, uint32_t
     g.col_blocks = (g.col_groups + 63) / 64;
     g.num_tiles = traces_vec_tiles(a.E, a.T, a.D, G, &g.chunks);
     g.jitter = jitter;
+    g.spins = spins;
     if (g.num_tiles >= ((int64_t)1 << 31))
         return set_error(RLSCAN_ERR_BAD_SHAPE, "too many tiles for one launch");
     const bool decay = a.decay != nullptr;

@@ -26,6 +26,7 @@ bool known_shape(int t, int w) {
 }
 
 std::atomic<uint32_t> g_jitter{0};  // look-back stress delay seed (0 = off)
+std::atomic<uint32_t> g_spins{kSpinLimit};  // polls before a look-back wait gives up
 std::atomic<int> g_shape{-1};  // tile << 4 | waves; -1 = not read from the environment yet
 
 int forced_shape() {
@@ -75,6 +76,7 @@ rlscan_status finish_plan(int64_t E, int64_t T, int tile, int waves, bool vec_ok
     plan.geo.interleave = (plan.lookback && E > 1 && T % tile == 0) ? 1 : 0;
     plan.geo.boost = 0;  // decided per kernel at launch
     plan.geo.jitter = g_jitter.load(std::memory_order_relaxed);
+    plan.geo.spins = g_spins.load(std::memory_order_relaxed);
     if (plan.geo.num_tiles >= kMaxTiles) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
     return RLSCAN_OK;
 }
@@ -170,6 +172,9 @@ rlscan_status plan_retrace(int64_t E, int64_t T, int64_t A, Plan& plan, bool vec
     } else if (retrace_pieces(A) > 0) {
         tile = 1024;  // 8 waves x 2 segments, slabs loaded up front
         waves = 8;
+    } else if (A > kRetraceStagedMaxActions) {
+        tile = 1024;  // rows reduced across the wave: 16 KiB of LDS per wave
+        waves = 4;
     } else {
         tile = 1024;  // 2*64*A floats of LDS per wave: one wave per workgroup
         waves = A > 32 ? 1 : 4;
@@ -239,6 +244,42 @@ rlscan_status set_error(rlscan_status st, const char* msg) {
     return st;
 }
 
+// Host-only part of a GAE call: argument checks and the launch plan.  No HIP
+// call is made before the checks pass (the planner reads the device's CU
+// count, cached).  `empty` is set for an empty batch, which launches nothing.
+rlscan_status gae_prepare(const float* rewards, const float* values, const float* terminateds,
+                          const float* truncateds, const float* bootstrap_values,
+                          const float* last_value, const float* skip, float* advantages,
+                          float* returns, int64_t num_envs, int64_t seq_len, float gamma,
+                          float lambda, GaeArgs& a, Plan& plan, bool& empty) {
+    empty = false;
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (std::isnan(gamma) || std::isnan(lambda)) return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN");
+    if (empty_batch(num_envs, seq_len)) {
+        empty = true;
+        return RLSCAN_OK;
+    }
+    RLSCAN_REQUIRE(rewards, "rewards");
+    RLSCAN_REQUIRE(values, "values");
+    RLSCAN_REQUIRE(terminateds, "terminateds");
+    RLSCAN_REQUIRE(advantages, "advantages");
+    if (last_value && bootstrap_values)
+        return set_error(RLSCAN_ERR_CONFLICT, "pass either last_value or bootstrap_values, not both");
+    if (last_value && truncateds)
+        return set_error(RLSCAN_ERR_CONFLICT, "last_value cannot be combined with truncateds; use bootstrap_values");
+    const bool vec = aligned16(rewards) && aligned16(values) && aligned16(terminateds) &&
+                     aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(advantages) &&
+                     aligned16(returns) && aligned16(skip);
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    a = GaeArgs{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+                advantages, returns, gamma, lambda, skip, nullptr};
+    return RLSCAN_OK;
+}
+
+size_t plan_workspace_bytes(const Plan& plan) {
+    return plan.lookback ? ws_bytes_for_tiles(plan.geo.num_tiles) : 0;
+}
+
 }  // namespace rlscan
 
 using namespace rlscan;
@@ -266,6 +307,10 @@ const char* rlscan_last_error(void) { return g_last_error; }
 size_t rlscan_workspace_bytes(int64_t num_envs, int64_t seq_len) {
     if (check_shape(num_envs, seq_len) != RLSCAN_OK || empty_batch(num_envs, seq_len)) return 0;
     const int64_t N = num_envs * seq_len;
+    // Every plan's tile is a multiple of kMinTile elements, so a batch of at
+    // most one such tile, or rows whose length divides it (every tile then
+    // holds whole rows), never takes a look-back.
+    if (N <= kMinTile || kMinTile % seq_len == 0) return 0;
     return ws_bytes_for_tiles((N + kMinTile - 1) / kMinTile);
 }
 
@@ -386,31 +431,21 @@ rlscan_status rlscan_check_inputs(const float* terminateds, const float* truncat
     return RLSCAN_OK;
 }
 
+
 namespace {
 rlscan_status gae_call(const float* rewards, const float* values, const float* terminateds,
                        const float* truncateds, const float* bootstrap_values,
                        const float* last_value, const float* skip, float* advantages,
                        float* returns, int64_t num_envs, int64_t seq_len, float gamma,
                        float lambda, void* ws, size_t ws_bytes, rlscan_stream_t stream) {
-    RLSCAN_TRY(check_shape(num_envs, seq_len));
-    if (std::isnan(gamma) || std::isnan(lambda)) return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda is NaN");
-    if (empty_batch(num_envs, seq_len)) return RLSCAN_OK;
-    RLSCAN_REQUIRE(rewards, "rewards");
-    RLSCAN_REQUIRE(values, "values");
-    RLSCAN_REQUIRE(terminateds, "terminateds");
-    RLSCAN_REQUIRE(advantages, "advantages");
-    if (last_value && bootstrap_values)
-        return set_error(RLSCAN_ERR_CONFLICT, "pass either last_value or bootstrap_values, not both");
-    if (last_value && truncateds)
-        return set_error(RLSCAN_ERR_CONFLICT, "last_value cannot be combined with truncateds; use bootstrap_values");
-    const bool vec = aligned16(rewards) && aligned16(values) && aligned16(terminateds) &&
-                     aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(advantages) &&
-                     aligned16(returns) && aligned16(skip);
+    GaeArgs a;
     Plan plan;
-    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    bool empty = false;
+    RLSCAN_TRY(gae_prepare(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+                           skip, advantages, returns, num_envs, seq_len, gamma, lambda, a, plan,
+                           empty));
+    if (empty) return RLSCAN_OK;
     RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
-    GaeArgs a{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
-              advantages, returns, gamma, lambda, skip};
     return launch_gae(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
 }
 }  // namespace
@@ -491,6 +526,7 @@ rlscan_status rlscan_traces_vec(const float* gradients, const float* decay, cons
     }
     VecTraceArgs a{gradients, decay, dones, seed, traces, num_envs, seq_len, dim, kappa};
     return launch_traces_vec(a, G, ws, g_jitter.load(std::memory_order_relaxed),
+                             g_spins.load(std::memory_order_relaxed),
                              reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -529,8 +565,10 @@ rlscan_status rlscan_retrace(const float* pi_target, const float* mu_taken, cons
                              int64_t num_actions, float gamma, float lambda, float c_bar,
                              float rho_bar, void* ws, size_t ws_bytes, rlscan_stream_t stream) {
     RLSCAN_TRY(check_shape(num_envs, seq_len));
-    if (num_actions < 1 || num_actions > 128)
-        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_actions must lie in [1, 128]");
+    if (num_actions < 1 || num_actions >= ((int64_t)1 << 31))
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_actions must lie in [1, 2^31)");
+    if (num_envs * seq_len > (((int64_t)1 << 46) / num_actions))
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len * num_actions too large");
     if (std::isnan(gamma) || std::isnan(lambda) || std::isnan(c_bar) || std::isnan(rho_bar))
         return set_error(RLSCAN_ERR_BAD_PARAM, "gamma/lambda/c_bar/rho_bar is NaN");
     if (empty_batch(num_envs, seq_len)) return RLSCAN_OK;
@@ -593,6 +631,11 @@ rlscan_status rlscan_prefix(const float* inputs, const float* dones, const float
 
 rlscan_status rlscan_debug_set_lookback_jitter(uint32_t seed) {
     g_jitter.store(seed, std::memory_order_relaxed);
+    return RLSCAN_OK;
+}
+
+rlscan_status rlscan_debug_set_spin_limit(uint32_t polls) {
+    g_spins.store(polls == 0 ? kSpinLimit : polls, std::memory_order_relaxed);
     return RLSCAN_OK;
 }
 

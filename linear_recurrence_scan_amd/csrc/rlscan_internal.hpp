@@ -68,6 +68,16 @@ struct Plan {
 
 rlscan_status set_error(rlscan_status st, const char* msg);
 
+// Argument checks and launch plan of a GAE call (host only; no HIP call
+// before the checks pass).  `empty`: an empty batch, nothing to launch.
+rlscan_status gae_prepare(const float* rewards, const float* values, const float* terminateds,
+                          const float* truncateds, const float* bootstrap_values,
+                          const float* last_value, const float* skip, float* advantages,
+                          float* returns, int64_t num_envs, int64_t seq_len, float gamma,
+                          float lambda, GaeArgs& a, Plan& plan, bool& empty);
+// Look-back workspace bytes a planned launch uses (0 without a look-back).
+size_t plan_workspace_bytes(const Plan& plan);
+
 // Rows shorter than the four-element lane group take one fixed launch shape
 // (2048 elements, 4 waves x 2 segments), with kernels built for it alone.
 constexpr int kShortRowTile = 2048;
@@ -83,7 +93,7 @@ struct VecTraceArgs {
 // Tiles of a launch with G columns per lane; *chunks receives the tiles per column block.
 int64_t traces_vec_tiles(int64_t E, int64_t T, int64_t D, int G, int64_t* chunks);
 rlscan_status launch_traces_vec(const VecTraceArgs& a, int G, void* ws, uint32_t jitter,
-                                hipStream_t s);
+                                uint32_t spins, hipStream_t s);
 
 rlscan_status launch_gae(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_gae_skip(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
@@ -97,6 +107,9 @@ rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, h
 // 16-byte pieces of each 3-D array a lane holds per segment for A actions (0:
 // each segment's slab is loaded when it is staged).
 int retrace_pieces(int64_t A);
+// Widest action set whose segment slab (2 x 64 x A floats) is staged whole in
+// a wave's LDS; wider sets reduce each step's row across the wave.
+constexpr int64_t kRetraceStagedMaxActions = 128;
 rlscan_status launch_returns(const ReturnsArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_prefix(const PrefixArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_fill_zero(void* p, size_t bytes, hipStream_t s);

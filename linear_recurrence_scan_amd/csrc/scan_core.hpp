@@ -130,6 +130,7 @@ struct Geo {
     int interleave;     // rows are whole multiples of the tile and tiles run column-major
     int boost;          // the whole grid is resident at once: issue loads at raised priority
     uint32_t jitter;    // nonzero: look-back stress test, seeded delay before each publication
+    uint32_t spins;     // polls a look-back wait makes before it gives up (kSpinLimit by default)
 };
 
 // Quotient of x / T for x < 2^31 using a precomputed reciprocal; exact after
@@ -351,7 +352,22 @@ struct WsHeader {
     static constexpr int kSlotsByteOffset = 256 + 64 * 64;
 };
 
+// Polls a look-back wait makes before it gives up, about a second of
+// waiting: far beyond any wait a correct launch produces, so reaching it
+// means a predecessor never published (a launch that broke the
+// forward-progress assumption, or a fault).  A tile that gives up takes a
+// NaN carry: its outputs, the inclusive value it publishes and every value
+// a later tile of the row derives from it are then NaN, so the failure shows
+// in the data instead of as plausible wrong numbers, and the sticky error
+// word of the workspace is set as well.
 constexpr uint32_t kSpinLimit = 1u << 22;
+
+__device__ __forceinline__ float timeout_carry() { return __builtin_nanf(""); }
+
+__device__ __forceinline__ void flag_timeout(uint8_t* ws) {
+    __hip_atomic_fetch_or(reinterpret_cast<uint32_t*>(ws) + WsHeader::kError, 1u,
+                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 __device__ __forceinline__ void slot_store(uint64_t* p, uint32_t tag, float v) {
     const uint64_t w = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
@@ -450,8 +466,19 @@ __device__ __forceinline__ bool lookback_resolve(const LookbackView& v, uint32_t
 // Every inclusive value is the same fixed function of the inputs whatever the
 // timing (the nesting always starts from the nearest published inclusive
 // value, and a tile publishes its inclusive value only once), so results are
-// bitwise reproducible.  Waits are bounded: past kSpinLimit polls the error
-// word is set and the tile proceeds with a zero carry.
+// bitwise reproducible.  Waits are bounded: past `spin_limit` polls the error
+// word is set and the tile proceeds with a NaN carry (see kSpinLimit).
+//
+// Forward progress.  Tile q = blockIdx.x waits only on tiles with smaller
+// block indices (q - stride, q - 2*stride, ...).  The assumption is the
+// hardware dispatcher's order: the workgroups a chiplet (XCD) receives start
+// in increasing block index, and a started workgroup keeps its slot until it
+// exits.  Take the unfinished tile with the smallest index, m.  Until m
+// starts, its chiplet starts nothing with a larger index, and every tile with
+// a smaller index has finished, so the chiplet has a free slot and m starts;
+// once started, m finds all its predecessors published.  By induction every
+// tile finishes, whatever the number of resident workgroups.  The bounded
+// wait is the guard if the assumption ever fails.
 // Stress-test delay (debug only): a bounded pseudo-random wait of 0 to 7
 // sleeps of 2048 cycles (up to about 6 microseconds), different per tile and
 // per seed, so that tiles publish in an order unrelated to their launch order.
@@ -466,10 +493,9 @@ __device__ __forceinline__ void jitter_delay(uint32_t seed, int64_t q) {
 
 __device__ __forceinline__ float lookback(uint8_t* ws, uint32_t epoch, int64_t q, int64_t stride,
                                           Affine tot, bool need_carry, uint64_t early,
-                                          uint32_t jitter = 0) {
+                                          uint32_t jitter, uint32_t spin_limit) {
     if (jitter) jitter_delay(jitter, q);
     uint64_t* slots = reinterpret_cast<uint64_t*>(ws + WsHeader::kSlotsByteOffset);
-    uint32_t* hdr = reinterpret_cast<uint32_t*>(ws);
     const uint32_t tag_agg = 2u * epoch + 1u;
     const uint32_t tag_inc = 2u * epoch + 2u;
     const int lane = lane_id();
@@ -489,11 +515,9 @@ __device__ __forceinline__ float lookback(uint8_t* ws, uint32_t epoch, int64_t q
         uint32_t spins = 0;
         for (;;) {
             if (lookback_resolve(lookback_read(ws, q, stride), epoch, x)) break;
-            if (++spins > kSpinLimit) {
-                if (lane == 0)
-                    __hip_atomic_fetch_or(hdr + WsHeader::kError, 1u, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-                x = 0.f;
+            if (++spins > spin_limit) {
+                if (lane == 0) flag_timeout(ws);
+                x = timeout_carry();
                 break;
             }
             __builtin_amdgcn_s_sleep(1);

@@ -13,7 +13,10 @@ Two layers, same names as the C ABI plus the reference-style helpers:
     eligibility_traces / episodic_prefix_sum: allocate outputs and follow the
     rl-triton keyword conventions (kernels page, API Reference).
 check_inputs runs the debug data checks (rlscan_check_inputs); with
-RLSCAN_CHECKS=1 in the environment every helper runs them before its call.
+RLSCAN_CHECKS=1 in the environment every helper runs them before its call,
+and every call reads back the look-back error word of its workspace
+afterwards, raising LookbackTimeout when a wait gave up (both synchronise
+the stream, so they are off by default).
 """
 from __future__ import annotations
 
@@ -48,6 +51,11 @@ class RLScanError(RuntimeError):
     def __init__(self, func, status, message):
         self.status = status
         super().__init__(f"{func} failed: status {status} ({message})")
+
+
+class LookbackTimeout(RuntimeError):
+    """A look-back wait of a call gave up: the workspace's error word is set
+    and the outputs that depend on the missing carry are NaN."""
 
 
 def lib():
@@ -90,20 +98,30 @@ def _declare(L):
     L.rlscan_debug_wave_scan.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
     L.rlscan_debug_set_launch_shape.argtypes = [ctypes.c_int, ctypes.c_int]
     L.rlscan_debug_set_lookback_jitter.argtypes = [ctypes.c_uint32]
+    L.rlscan_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
     L.rlscan_check_inputs.argtypes = [vp] * 4 + [i64, i64, i64, vp, sz,
                                                  ctypes.POINTER(CheckReport), vp]
     for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
-                 "rlscan_gae_norm", "rlscan_traces_vec", "rlscan_gae", "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
+                 "rlscan_gae_norm", "rlscan_traces_vec", "rlscan_gae",
+                 "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
                  "rlscan_check_inputs", "rlscan_debug_set_launch_shape",
-                 "rlscan_debug_set_lookback_jitter"):
+                 "rlscan_debug_set_lookback_jitter", "rlscan_debug_set_spin_limit"):
         getattr(L, name).restype = st
     return L
 
 
-def _check(func, status):
+def _check(func, status, device=None):
+    """Raises on a non-OK status.  With RLSCAN_CHECKS=1 and a `device`, also
+    reads back the error word of the call's workspace and raises
+    LookbackTimeout when it is set."""
     if status != RLSCAN_OK:
         msg = lib().rlscan_last_error().decode(errors="replace")
         raise RLScanError(func, status, msg)
+    if device is not None and _checks_enabled():
+        err = workspace_error(device)
+        if err:
+            raise LookbackTimeout(f"{func}: a look-back wait exceeded its bound (error word "
+                                  f"{err:#x}); outputs that depend on the missing carry are NaN")
 
 
 def _ptr(t):
@@ -183,6 +201,17 @@ def workspace_error(device=None):
     return int(out.value)
 
 
+def reset_workspace(device=None):
+    """Zero-fills the current stream's cached workspace again (clears the
+    sticky error word and all look-back state); a no-op when there is none."""
+    device = torch.device(device if device is not None else torch.cuda.current_device())
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is not None:
+        _check("rlscan_workspace_init", lib().rlscan_workspace_init(_ptr(ws), ws.numel(),
+                                                                    _stream(device)))
+
+
 def check_inputs(terminateds=None, truncateds=None, bootstrap_values=None, actions=None,
                  num_actions=0):
     """Runs rlscan_check_inputs (synchronous) and returns its counts as a dict
@@ -241,7 +270,7 @@ def rlscan_gae(rewards, values, terminateds, truncateds, bootstrap_values, last_
     st = lib().rlscan_gae(_ptr(rewards), _ptr(values), _ptr(terminateds), _ptr(truncateds),
                           _ptr(bootstrap_values), _ptr(last_value), _ptr(advantages), _ptr(returns),
                           E, T, float(gamma), float(lambda_), _ptr(ws), nws, _stream(dev))
-    _check("rlscan_gae", st)
+    _check("rlscan_gae", st, dev)
 
 
 def rlscan_gae_norm(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
@@ -253,7 +282,7 @@ def rlscan_gae_norm(rewards, values, terminateds, truncateds, bootstrap_values, 
                                _ptr(bootstrap_values), _ptr(last_value), _ptr(advantages),
                                _ptr(returns), _ptr(stats), E, T, float(gamma), float(lambda_),
                                float(eps), _ptr(ws), nws, _stream(dev))
-    _check("rlscan_gae_norm", st)
+    _check("rlscan_gae_norm", st, dev)
 
 
 def rlscan_traces_vec(gradients, decay, dones, seed_values, traces, kappa):
@@ -262,7 +291,7 @@ def rlscan_traces_vec(gradients, decay, dones, seed_values, traces, kappa):
     ws, nws = workspace(dev, E, T, int(lib().rlscan_traces_vec_workspace_bytes(E, T, D)))
     st = lib().rlscan_traces_vec(_ptr(gradients), _ptr(decay), _ptr(dones), _ptr(seed_values),
                                  _ptr(traces), E, T, D, float(kappa), _ptr(ws), nws, _stream(dev))
-    _check("rlscan_traces_vec", st)
+    _check("rlscan_traces_vec", st, dev)
 
 
 def rlscan_gae_skip(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
@@ -274,7 +303,7 @@ def rlscan_gae_skip(rewards, values, terminateds, truncateds, bootstrap_values, 
                                _ptr(bootstrap_values), _ptr(last_value), _ptr(skip_mask),
                                _ptr(advantages), _ptr(returns), E, T, float(gamma), float(lambda_),
                                _ptr(ws), nws, _stream(dev))
-    _check("rlscan_gae_skip", st)
+    _check("rlscan_gae_skip", st, dev)
 
 
 def rlscan_gae_bf16(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
@@ -286,7 +315,7 @@ def rlscan_gae_bf16(rewards, values, terminateds, truncateds, bootstrap_values, 
                                _ptr(bootstrap_values), _ptr(last_value), _ptr(advantages),
                                _ptr(returns), E, T, float(gamma), float(lambda_), _ptr(ws), nws,
                                _stream(dev))
-    _check("rlscan_gae_bf16", st)
+    _check("rlscan_gae_bf16", st, dev)
 
 
 def rlscan_vtrace(log_pi_target, log_pi_behavior, values, rewards, terminateds, truncateds,
@@ -298,7 +327,7 @@ def rlscan_vtrace(log_pi_target, log_pi_behavior, values, rewards, terminateds, 
                              _ptr(terminateds), _ptr(truncateds), _ptr(bootstrap_values),
                              _ptr(last_value), _ptr(vs), _ptr(pg_advantages), E, T, float(gamma),
                              float(rho_bar), float(c_bar), _ptr(ws), nws, _stream(dev))
-    _check("rlscan_vtrace", st)
+    _check("rlscan_vtrace", st, dev)
 
 
 def rlscan_retrace(pi_target, mu_taken, q_taken, next_q_all, actions, rewards, terminateds,
@@ -311,7 +340,7 @@ def rlscan_retrace(pi_target, mu_taken, q_taken, next_q_all, actions, rewards, t
                               _ptr(actions), _ptr(rewards), _ptr(terminateds), _ptr(truncateds),
                               _ptr(q_ret), _ptr(advantages), E, T, A, float(gamma), float(lambda_),
                               float(c_bar), float(rho_bar), _ptr(ws), nws, _stream(dev))
-    _check("rlscan_retrace", st)
+    _check("rlscan_retrace", st, dev)
 
 
 def rlscan_returns(rewards, next_values, terminateds, truncateds, bootstrap_values, out, gamma,
@@ -322,7 +351,7 @@ def rlscan_returns(rewards, next_values, terminateds, truncateds, bootstrap_valu
     st = lib().rlscan_returns(_ptr(rewards), _ptr(next_values), _ptr(terminateds), _ptr(truncateds),
                               _ptr(bootstrap_values), _ptr(out), E, T, float(gamma), float(lambda_),
                               _ptr(ws), nws, _stream(dev))
-    _check("rlscan_returns", st)
+    _check("rlscan_returns", st, dev)
 
 
 def rlscan_prefix(inputs, dones, seed, out, decay, boundary):
@@ -332,7 +361,7 @@ def rlscan_prefix(inputs, dones, seed, out, decay, boundary):
     b = {"ends_at": RLSCAN_ENDS_AT, "starts_at": RLSCAN_STARTS_AT}.get(boundary, boundary)
     st = lib().rlscan_prefix(_ptr(inputs), _ptr(dones), _ptr(seed), _ptr(out), E, T, float(decay),
                              int(b), _ptr(ws), nws, _stream(dev))
-    _check("rlscan_prefix", st)
+    _check("rlscan_prefix", st, dev)
 
 
 LAUNCH_SHAPES = ((256, 1), (1024, 2), (2048, 4), (4096, 4), (4096, 8))
@@ -342,6 +371,12 @@ def set_launch_shape(tile=0, waves=0):
     """Forces the launch shape of the four-elements-per-lane scans ((0, 0):
     the planner's choice); see include/rlscan_debug.h."""
     _check("rlscan_debug_set_launch_shape", lib().rlscan_debug_set_launch_shape(int(tile), int(waves)))
+
+
+def set_spin_limit(polls=0):
+    """Bound of every look-back wait in polls (0 = the default); see
+    include/rlscan_debug.h."""
+    _check("rlscan_debug_set_spin_limit", lib().rlscan_debug_set_spin_limit(int(polls)))
 
 
 def set_lookback_jitter(seed=0):

@@ -56,10 +56,25 @@ def test_abi_version_and_strings(L):
 def test_workspace_bytes(L):
     assert L.rlscan_workspace_bytes(0, 10) == 0
     assert L.rlscan_workspace_bytes(10, 0) == 0
-    small = L.rlscan_workspace_bytes(1, 1)
-    assert small >= 256
+    assert L.rlscan_workspace_bytes(-1, 10) == 0
+    # every row fits one tile: at most 256 steps in all, or a row length that
+    # divides the 256-step tile (every tile then holds whole rows)
+    for E, T in ((1, 1), (1, 200), (3, 80), (100000, 2), (4096, 4), (1000, 128), (4096, 256)):
+        assert L.rlscan_workspace_bytes(E, T) == 0, (E, T)
+    # rows that straddle tiles, or span several
+    for E, T in ((2, 200), (1, 257), (100, 3), (4096, 1000), (4096, 1024), (8, 512)):
+        assert L.rlscan_workspace_bytes(E, T) > 4352, (E, T)
     big = L.rlscan_workspace_bytes(64, 131072)
     assert big >= 256 + 32 * (64 * 131072 // 1024)
+
+
+def test_shapes_needing_no_workspace_are_accepted_without_one(L):
+    # NULL workspace: the look-back is off at these shapes, so argument
+    # checking passes the workspace check (an invalid gamma then stops the
+    # call before any HIP call)
+    for E, T in ((3, 80), (4096, 4), (1000, 128), (4096, 256)):
+        assert L.rlscan_workspace_bytes(E, T) == 0
+        assert L.rlscan_gae(P, P, P, N, N, N, P, N, E, T, float("nan"), 0.95, N, 0, N) == BAD_PARAM
 
 
 def gae(L, r=P, v=P, te=P, tr=N, bv=N, lv=N, adv=P, ret=N, E=4, T=8, ws=N, nws=0):
@@ -188,9 +203,14 @@ def test_retrace_validation(L):
     for kw in ("pi", "mu", "q", "qn", "act", "r", "te", "qr"):
         assert call(**{kw: N}) == NULL_ARG, kw
     assert call(A=0) == BAD_SHAPE
-    assert call(A=129) == BAD_SHAPE
+    assert call(A=-5) == BAD_SHAPE
+    assert call(A=1 << 31) == BAD_SHAPE
+    assert call(E=1 << 20, T=1 << 16, A=1 << 11) == BAD_SHAPE   # E*T*A > 2^46
     assert call(E=0) == OK
     assert call(E=0, A=0) == BAD_SHAPE
+    assert call(E=0, A=129) == OK       # no cap on the action count
+    assert call(E=0, A=100000) == OK
+    assert call(E=4096, T=1000, A=1000) == WORKSPACE   # past argument checks, needs a workspace
 
 
 def test_returns_and_prefix_validation(L):
@@ -217,6 +237,12 @@ def test_check_inputs_validation(L):
     assert call(ws=ctypes.c_void_p(0x100040)) == WORKSPACE
     assert call(nws=1000) == WORKSPACE
     assert b"workspace" in L.rlscan_last_error()
+
+
+def test_spin_limit_switch(L):
+    L.rlscan_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
+    assert L.rlscan_debug_set_spin_limit(5) == OK
+    assert L.rlscan_debug_set_spin_limit(0) == OK   # back to the default bound
 
 
 def test_launch_shape_override_validation(L):

@@ -332,6 +332,13 @@ RETRACE_CASES = [
     (20, 4000, 21, 0.01),   # A = 21: 8 pieces per lane
     (40, 2500, 25, 0.01),
     (9, 8000, 40, 0.01),    # A > 32: slabs staged per segment
+    # A > 128: each step's row reduced across the wave
+    (3, 500, 129, 0.01),
+    (4, 300, 130, 0.01),    # rows not 16-byte aligned: per-entry loads
+    (6, 700, 256, 0.01),
+    (2, 400, 1000, 0.02),
+    (70, 1000, 200, 0.01),  # above 64K steps: 4-wave tiles, rows straddle tiles
+    (1, 70, 4099, 0.0),     # a ragged single segment
 ]
 
 
@@ -352,6 +359,29 @@ def test_retrace_unaligned_3d_arrays():
     per-element path; results are the same."""
     E, T, A = 40, 2000, 18
     d = synth.retrace_inputs(E, T, A, seed=77, p_term=0.01)
+    args = (d["pi_target"], d["mu_taken"], d["q_taken"], d["next_q_all"], d["actions"],
+            d["rewards"], d["terminateds"], None)
+    want_q, want_adv = oracle.retrace(*args, f32(0.99), f32(0.95), 1.0, 1.0)
+
+    def shifted(x):
+        buf = torch.empty(x.size + 1, dtype=torch.float32, device="cuda")
+        view = buf[1:].view(x.shape)
+        view.copy_(torch.from_numpy(x))
+        assert view.data_ptr() % 16 != 0
+        return view
+    g = [dev(x) for x in args[:7]]
+    g[0], g[3] = shifted(d["pi_target"]), shifted(d["next_q_all"])
+    q, adv = ops.retrace(*g, None, 0.99, 0.95, 1.0, 1.0)
+    assert_close(q, want_q, T, "q_ret")
+    assert_close(adv, want_adv, T, "advantages")
+
+
+@pytest.mark.parametrize("A", [256, 131])
+def test_retrace_wide_unaligned_3d_arrays(A):
+    """Wide action sets with 3-D arrays that are not 16-byte aligned: every
+    row is read entry by entry."""
+    E, T = 20, 3500
+    d = synth.retrace_inputs(E, T, A, seed=78 + A, p_term=0.01)
     args = (d["pi_target"], d["mu_taken"], d["q_taken"], d["next_q_all"], d["actions"],
             d["rewards"], d["terminateds"], None)
     want_q, want_adv = oracle.retrace(*args, f32(0.99), f32(0.95), 1.0, 1.0)
