@@ -173,6 +173,29 @@ rlscan_status rlscan_gae(const float* rewards, const float* values, const float*
                          void* ws, size_t ws_bytes, rlscan_stream_t stream);
 
 /*
+ * rlscan_gae without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, results, NULL rules, conflicts and
+ * errors are those of rlscan_gae; the call allocates nothing.  Its look-back
+ * state lives in a 2 MiB static device array of the library: each GPU holds
+ * its own copy from the first call on that GPU (which zero-fills it on
+ * `stream`) until the process ends.  Every call on one GPU shares that array
+ * and it keeps the last call's contents (each call leaves it ready for the
+ * next, as a workspace), so calls that overlap on one GPU -- on different
+ * streams, or from different threads without ordering -- race and must not
+ * be issued.  Shapes whose look-back needs more than the array holds (over
+ * 65,400 tiles, about 268 million steps) return BAD_SHAPE before any HIP
+ * call.  The array's error word cannot be read back; a look-back wait that
+ * gives up still shows as NaN outputs.
+ */
+rlscan_status rlscan_gae_noalloc(const float* rewards, const float* values,
+                                 const float* terminateds, const float* truncateds,
+                                 const float* bootstrap_values, const float* last_value,
+                                 float* advantages, float* returns, int64_t num_envs,
+                                 int64_t seq_len, float gamma, float lambda,
+                                 rlscan_stream_t stream);
+
+/*
  * GAE with batch advantage normalisation -- paper Sec. 9.3 plans fused
  * advantage normalisation; the formula is the usual whitening of PPO
  * advantages, over all E*T steps of the call:

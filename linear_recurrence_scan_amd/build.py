@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librlscan.so")
 HIP_SOURCES = ["op_gae.hip", "op_gae_skip.hip", "op_gae_compact.hip", "op_gae_norm.hip", "op_vtrace.hip", "op_vtrace_clip.hip", "op_returns.hip",
-               "op_prefix.hip", "op_retrace.hip", "op_traces_vec.hip", "aux_kernels.hip"]
+               "op_prefix.hip", "op_retrace.hip", "op_traces_vec.hip", "aux_kernels.hip",
+               "noalloc.hip"]
 HOST_SOURCES = ["rlscan_api.cpp"]
 ARCH = os.environ.get("RLSCAN_OFFLOAD_ARCH", "gfx950")
 

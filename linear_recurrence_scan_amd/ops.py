@@ -83,6 +83,7 @@ def _declare(L):
     L.rlscan_workspace_init.argtypes = [vp, sz, vp]
     L.rlscan_workspace_error.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
     L.rlscan_gae.argtypes = [vp] * 8 + [i64, i64, f32, f32, vp, sz, vp]
+    L.rlscan_gae_noalloc.argtypes = [vp] * 8 + [i64, i64, f32, f32, vp]
     L.rlscan_gae_norm.argtypes = [vp] * 9 + [i64, i64, f32, f32, f32, vp, sz, vp]
     L.rlscan_gae_norm_workspace_bytes.argtypes = [i64, i64]
     L.rlscan_gae_norm_workspace_bytes.restype = sz
@@ -102,7 +103,7 @@ def _declare(L):
     L.rlscan_check_inputs.argtypes = [vp] * 4 + [i64, i64, i64, vp, sz,
                                                  ctypes.POINTER(CheckReport), vp]
     for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
-                 "rlscan_gae_norm", "rlscan_traces_vec", "rlscan_gae",
+                 "rlscan_gae_norm", "rlscan_traces_vec", "rlscan_gae", "rlscan_gae_noalloc",
                  "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
                  "rlscan_check_inputs", "rlscan_debug_set_launch_shape",
                  "rlscan_debug_set_lookback_jitter", "rlscan_debug_set_spin_limit"):
@@ -271,6 +272,19 @@ def rlscan_gae(rewards, values, terminateds, truncateds, bootstrap_values, last_
                           _ptr(bootstrap_values), _ptr(last_value), _ptr(advantages), _ptr(returns),
                           E, T, float(gamma), float(lambda_), _ptr(ws), nws, _stream(dev))
     _check("rlscan_gae", st, dev)
+
+
+def rlscan_gae_noalloc(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
+                       advantages, returns, gamma, lambda_):
+    """rlscan_gae without a workspace: the library's static per-device scratch
+    holds the look-back state, and nothing is allocated (calls that overlap
+    on one GPU race; see include/rlscan.h)."""
+    E, T = _shape2("rewards", rewards)
+    dev = rewards.device
+    st = lib().rlscan_gae_noalloc(_ptr(rewards), _ptr(values), _ptr(terminateds), _ptr(truncateds),
+                                  _ptr(bootstrap_values), _ptr(last_value), _ptr(advantages),
+                                  _ptr(returns), E, T, float(gamma), float(lambda_), _stream(dev))
+    _check("rlscan_gae_noalloc", st)
 
 
 def rlscan_gae_norm(rewards, values, terminateds, truncateds, bootstrap_values, last_value,
