@@ -41,6 +41,37 @@ rlscan_status rlscan_debug_set_launch_shape(int tile, int waves);
  * while no other thread is calling the library.  Always returns RLSCAN_OK. */
 rlscan_status rlscan_debug_set_lookback_jitter(uint32_t seed);
 
+/* Streaming reference for roofline context: reads num_inputs fp32 arrays and
+ * writes num_outputs fp32 arrays of n elements each (outputs[o][i] = the sum
+ * of inputs[.][i]), with the access pattern and launch shape of the scan
+ * kernels (512-thread workgroups over 4096-element tiles, 16-byte
+ * non-temporal loads all issued before any store) and no scan.  Its duration
+ * is what the memory system delivers to that pattern; a scan kernel moving
+ * the same arrays can be compared with it.  (num_inputs, num_outputs) is one
+ * of (1,1), (2,1), (3,1), (4,1), (4,2), (5,2), (6,2).  `inputs` and `outputs`
+ * are HOST arrays of DEVICE pointers, each 16-byte aligned.
+ * Errors: NULL arrays or entries -> NULL_ARG; an unsupported pair or a
+ * misaligned array -> BAD_PARAM; n not a positive multiple of 4096 ->
+ * BAD_SHAPE. */
+rlscan_status rlscan_debug_stream(const float* const* inputs, int num_inputs,
+                                  float* const* outputs, int num_outputs, int64_t n,
+                                  rlscan_stream_t stream);
+
+/* Per-tile phase stamps, for profiling the look-back: in a library built
+ * with RLSCAN_PHASE_STAMPS (librlscan_stamps.so), every later launch of the
+ * scans of GAE, V-trace, Retrace, returns and the forward recurrences writes,
+ * for each tile q < max_tiles (q = the workgroup index), the GPU's 100 MHz
+ * constant clock at six phases to stamps[8q + k]: k = 0 tile start, 1 loads
+ * issued, 2 the first wave's segments loaded and scanned, 3 the workgroup's
+ * total known, 4 the carry into the tile known (after the look-back), 5 the
+ * outputs' stores issued; entries 6 and 7 are left alone.  `stamps` is a
+ * DEVICE array of 8 * max_tiles uint64 (8-byte aligned); NULL turns stamping
+ * off.  Other builds return BAD_PARAM for a non-NULL buffer and report 0 from
+ * rlscan_debug_phase_stamps_built.  Process-wide; set it while no other
+ * thread is calling the library. */
+int rlscan_debug_phase_stamps_built(void);
+rlscan_status rlscan_debug_set_phase_stamps(uint64_t* stamps, int64_t max_tiles);
+
 /* Bound of every look-back wait, in polls, for every later call in the
  * process; 0 restores the default (about a second of waiting).  A wait that
  * reaches the bound gives up: the tile takes a NaN carry, so its outputs and

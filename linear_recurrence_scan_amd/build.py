@@ -17,6 +17,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librlscan.so")
+# The same library with per-tile phase stamps compiled in (profiling only).
+STAMPS_LIB = os.path.join(HERE, "librlscan_stamps.so")
 HIP_SOURCES = ["op_gae.hip", "op_gae_skip.hip", "op_gae_compact.hip", "op_gae_norm.hip", "op_vtrace.hip", "op_vtrace_clip.hip", "op_returns.hip",
                "op_prefix.hip", "op_retrace.hip", "op_traces_vec.hip", "aux_kernels.hip",
                "noalloc.hip"]
@@ -72,5 +74,12 @@ def build(verbose: bool = False, out: str = LIB, defines=(), csrc: str = CSRC) -
     return out
 
 
+def build_stamps(verbose: bool = False) -> str:
+    """Builds librlscan_stamps.so: the library with RLSCAN_PHASE_STAMPS."""
+    return build(verbose=verbose, out=STAMPS_LIB, defines=("RLSCAN_PHASE_STAMPS",))
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    if "--stamps" in sys.argv:
+        print(build_stamps(verbose="-v" in sys.argv))

@@ -51,6 +51,65 @@ __global__ void check_kernel(const float* term, const float* trunc, const float*
     if (threadIdx.x < 4 && s_counts[threadIdx.x]) atomicAdd(&counts[threadIdx.x], s_counts[threadIdx.x]);
 }
 
+// Streaming reference for the roofline context: NIN fp32 arrays read and
+// NOUT written per element, with the scan kernels' access pattern and launch
+// shape but no scan (512-thread workgroups, tiles of two 1 KiB-per-wave
+// segments, 16-byte non-temporal loads all issued before any store, the same
+// pause between segments, plain 16-byte stores).  Its time for a workload's
+// arrays is what the memory system gives that pattern on this device.
+constexpr int kStreamMax = 6;
+constexpr int kStreamTile = 4096;
+struct StreamPtrs {
+    const float* in[kStreamMax];
+    float* out[kStreamMax];
+};
+
+template <int NIN, int NOUT>
+__global__ __launch_bounds__(512) void stream_kernel(StreamPtrs p) {
+    const size_t base = (size_t)blockIdx.x * kStreamTile + threadIdx.x * 4;  // segment 0
+    f32x4 v[2][NIN];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int a = 0; a < NIN; ++a) v[s][a] = load16(p.in[a] + base + s * (kStreamTile / 2));
+        if (s == 0) __builtin_amdgcn_s_sleep(4);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        f32x4 acc = v[s][0];
+#pragma unroll
+        for (int a = 1; a < NIN; ++a) acc += v[s][a];
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) store16(p.out[o] + base + s * (kStreamTile / 2), acc);
+    }
+}
+
+template <int NIN, int NOUT>
+static void launch_stream_n(const StreamPtrs& p, int64_t n, hipStream_t s) {
+    hipLaunchKernelGGL((stream_kernel<NIN, NOUT>), dim3((unsigned)(n / kStreamTile)), dim3(512), 0,
+                       s, p);
+}
+
+rlscan_status launch_debug_stream(const float* const* in, int nin, float* const* out, int nout,
+                                  int64_t n, hipStream_t s) {
+    StreamPtrs p{};
+    for (int a = 0; a < nin; ++a) p.in[a] = in[a];
+    for (int o = 0; o < nout; ++o) p.out[o] = out[o];
+    switch (nin * 10 + nout) {
+        case 11: launch_stream_n<1, 1>(p, n, s); break;
+        case 21: launch_stream_n<2, 1>(p, n, s); break;
+        case 31: launch_stream_n<3, 1>(p, n, s); break;
+        case 41: launch_stream_n<4, 1>(p, n, s); break;
+        case 42: launch_stream_n<4, 2>(p, n, s); break;
+        case 52: launch_stream_n<5, 2>(p, n, s); break;
+        case 62: launch_stream_n<6, 2>(p, n, s); break;
+        default: return set_error(RLSCAN_ERR_BAD_PARAM, "unsupported number of input/output arrays");
+    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return set_error(RLSCAN_ERR_LAUNCH, hipGetErrorString(err));
+    return RLSCAN_OK;
+}
+
 rlscan_status launch_debug_wave_scan(const float* a, const float* b, float* oa, float* ob,
                                      int num_waves, hipStream_t s) {
     hipLaunchKernelGGL(debug_wave_scan_kernel, dim3((unsigned)num_waves), dim3(kWave), 0, s, a, b,

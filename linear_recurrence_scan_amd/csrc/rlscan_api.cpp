@@ -27,6 +27,8 @@ bool known_shape(int t, int w) {
 
 std::atomic<uint32_t> g_jitter{0};  // look-back stress delay seed (0 = off)
 std::atomic<uint32_t> g_spins{kSpinLimit};  // polls before a look-back wait gives up
+std::atomic<uint64_t*> g_stamps{nullptr};    // phase-stamp buffer (profiling builds)
+std::atomic<int64_t> g_stamp_tiles{0};
 std::atomic<int> g_shape{-1};  // tile << 4 | waves; -1 = not read from the environment yet
 
 int forced_shape() {
@@ -77,6 +79,8 @@ rlscan_status finish_plan(int64_t E, int64_t T, int tile, int waves, bool vec_ok
     plan.geo.boost = 0;  // decided per kernel at launch
     plan.geo.jitter = g_jitter.load(std::memory_order_relaxed);
     plan.geo.spins = g_spins.load(std::memory_order_relaxed);
+    plan.geo.stamps = g_stamps.load(std::memory_order_relaxed);
+    plan.geo.stamp_tiles = g_stamp_tiles.load(std::memory_order_relaxed);
     if (plan.geo.num_tiles >= kMaxTiles) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs * seq_len too large");
     return RLSCAN_OK;
 }
@@ -634,6 +638,25 @@ rlscan_status rlscan_debug_set_lookback_jitter(uint32_t seed) {
     return RLSCAN_OK;
 }
 
+int rlscan_debug_phase_stamps_built(void) {
+#ifdef RLSCAN_PHASE_STAMPS
+    return 1;
+#else
+    return 0;
+#endif
+}
+
+rlscan_status rlscan_debug_set_phase_stamps(uint64_t* stamps, int64_t max_tiles) {
+    if (stamps && !rlscan_debug_phase_stamps_built())
+        return set_error(RLSCAN_ERR_BAD_PARAM, "this build records no phase stamps (build with RLSCAN_PHASE_STAMPS)");
+    if (stamps && max_tiles < 1) return set_error(RLSCAN_ERR_BAD_SHAPE, "max_tiles must be >= 1");
+    if (stamps && (reinterpret_cast<uintptr_t>(stamps) & 7u) != 0)
+        return set_error(RLSCAN_ERR_BAD_PARAM, "stamps must be 8-byte aligned");
+    g_stamps.store(stamps, std::memory_order_relaxed);
+    g_stamp_tiles.store(stamps ? max_tiles : 0, std::memory_order_relaxed);
+    return RLSCAN_OK;
+}
+
 rlscan_status rlscan_debug_set_spin_limit(uint32_t polls) {
     g_spins.store(polls == 0 ? kSpinLimit : polls, std::memory_order_relaxed);
     return RLSCAN_OK;
@@ -648,6 +671,29 @@ rlscan_status rlscan_debug_set_launch_shape(int tile, int waves) {
         return set_error(RLSCAN_ERR_BAD_PARAM, "unknown launch shape (see rlscan_debug.h)");
     g_shape.store(tile << 4 | waves, std::memory_order_relaxed);
     return RLSCAN_OK;
+}
+
+rlscan_status rlscan_debug_stream(const float* const* inputs, int num_inputs,
+                                  float* const* outputs, int num_outputs, int64_t n,
+                                  rlscan_stream_t stream) {
+    RLSCAN_REQUIRE(inputs, "inputs");
+    RLSCAN_REQUIRE(outputs, "outputs");
+    static const int kPairs[][2] = {{1, 1}, {2, 1}, {3, 1}, {4, 1}, {4, 2}, {5, 2}, {6, 2}};
+    bool known = false;
+    for (const auto& pr : kPairs) known = known || (pr[0] == num_inputs && pr[1] == num_outputs);
+    if (!known) return set_error(RLSCAN_ERR_BAD_PARAM, "unsupported number of input/output arrays");
+    if (n <= 0 || n % 4096 != 0 || n / 4096 >= ((int64_t)1 << 31))
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "n must be a positive multiple of 4096");
+    for (int a = 0; a < num_inputs; ++a) {
+        RLSCAN_REQUIRE(inputs[a], "inputs[i]");
+        if (!aligned16(inputs[a])) return set_error(RLSCAN_ERR_BAD_PARAM, "arrays must be 16-byte aligned");
+    }
+    for (int o = 0; o < num_outputs; ++o) {
+        RLSCAN_REQUIRE(outputs[o], "outputs[i]");
+        if (!aligned16(outputs[o])) return set_error(RLSCAN_ERR_BAD_PARAM, "arrays must be 16-byte aligned");
+    }
+    return launch_debug_stream(inputs, num_inputs, outputs, num_outputs, n,
+                               reinterpret_cast<hipStream_t>(stream));
 }
 
 rlscan_status rlscan_debug_wave_scan(const float* a, const float* b, float* out_a, float* out_b,

@@ -118,6 +118,8 @@ rlscan_status launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 rlscan_status launch_check(const float* term, const float* trunc, const float* boot,
                            const int64_t* actions, int64_t N, int64_t T, int64_t A,
                            unsigned long long* counts, hipStream_t s);
+rlscan_status launch_debug_stream(const float* const* in, int nin, float* const* out, int nout,
+                                  int64_t n, hipStream_t s);
 rlscan_status launch_debug_wave_scan(const float* a, const float* b, float* oa, float* ob,
                                     int num_waves, hipStream_t s);
 

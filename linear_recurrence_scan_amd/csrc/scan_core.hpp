@@ -131,6 +131,8 @@ struct Geo {
     int boost;          // the whole grid is resident at once: issue loads at raised priority
     uint32_t jitter;    // nonzero: look-back stress test, seeded delay before each publication
     uint32_t spins;     // polls a look-back wait makes before it gives up (kSpinLimit by default)
+    uint64_t* stamps;   // phase stamps of each tile (profiling builds only), or null
+    int64_t stamp_tiles;  // tiles the stamp buffer holds
 };
 
 // Quotient of x / T for x < 2^31 using a precomputed reciprocal; exact after

@@ -37,6 +37,17 @@
 
 namespace rlscan {
 
+// Phase stamps (profiling builds, RLSCAN_PHASE_STAMPS): thread 0 of tile q
+// writes the 100 MHz constant clock to stamps[8q + k] at phase k: 0 entry,
+// 1 loads issued, 2 first segment's data in and scanned, 3 workgroup total
+// known, 4 carry known, 5 stores issued.  Other builds compile it away.
+__device__ __forceinline__ void stamp(const Geo& g, int64_t q, int k) {
+#ifdef RLSCAN_PHASE_STAMPS
+    if (g.stamps && threadIdx.x == 0 && q < g.stamp_tiles)
+        g.stamps[8 * q + k] = __builtin_amdgcn_s_memrealtime();
+#endif
+}
+
 // Inputs a call may omit.  Each Op is compiled once per combination it
 // supports, so an absent stream costs neither a load nor a register.
 enum : unsigned {
@@ -202,6 +213,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
     }
 
     if (g.boost) __builtin_amdgcn_s_setprio(0);
+    stamp(g, q, 1);
 
     // A tile whose first scan element starts a row segment needs no carry.
     bool need_carry = false;
@@ -240,6 +252,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
         segtot[s] = Affine{readlane(incl[s].a, kWave - 1), readlane(incl[s].b, kWave - 1)};
     }
 
+    stamp(g, q, 2);
     Affine wtot = segtot[0];
 #pragma unroll
     for (int s = 1; s < SEGS; ++s) wtot = compose(segtot[s], wtot);
@@ -262,6 +275,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
         ttot = acc;
     }
 
+    stamp(g, q, 3);
     // across workgroups
     float x = 0.f;
     if constexpr (LOOKBACK) {
@@ -284,6 +298,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
         }
     }
 
+    stamp(g, q, 4);
     // phase 3: apply the carries and write the outputs
     constexpr bool kStats = WantsStats<Op>::value;
     Stat st{0.f, 0.f, 0.f};
@@ -319,6 +334,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
             st = stat_merge(st, Stat{n, m, m2});
         }
     }
+    stamp(g, q, 5);
     if constexpr (kStats) {
         // lanes: butterfly merges (a fixed pattern, so the result is
         // reproducible); waves: merged in order by thread 0
@@ -368,6 +384,7 @@ __attribute__((amdgpu_waves_per_eu(WavesPerEu<Op, SEGS, LOOKBACK>::value))) void
     extern __shared__ __align__(16) float s_dyn[];
 
     const int64_t q = blockIdx.x;  // tile index in scan order
+    stamp(g, q, 0);
     // Every tile of a look-back launch takes its epoch ticket first; the add
     // completes while the tile's data loads are in flight.
     uint64_t ticket = 0;

@@ -100,13 +100,18 @@ def _declare(L):
     L.rlscan_debug_set_launch_shape.argtypes = [ctypes.c_int, ctypes.c_int]
     L.rlscan_debug_set_lookback_jitter.argtypes = [ctypes.c_uint32]
     L.rlscan_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
+    L.rlscan_debug_set_phase_stamps.argtypes = [vp, i64]
+    L.rlscan_debug_phase_stamps_built.restype = ctypes.c_int
+    L.rlscan_debug_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
+                                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, i64, vp]
     L.rlscan_check_inputs.argtypes = [vp] * 4 + [i64, i64, i64, vp, sz,
                                                  ctypes.POINTER(CheckReport), vp]
     for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
                  "rlscan_gae_norm", "rlscan_traces_vec", "rlscan_gae", "rlscan_gae_noalloc",
                  "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
                  "rlscan_check_inputs", "rlscan_debug_set_launch_shape",
-                 "rlscan_debug_set_lookback_jitter", "rlscan_debug_set_spin_limit"):
+                 "rlscan_debug_set_lookback_jitter", "rlscan_debug_set_spin_limit",
+                 "rlscan_debug_stream", "rlscan_debug_set_phase_stamps"):
         getattr(L, name).restype = st
     return L
 
@@ -396,6 +401,17 @@ def set_spin_limit(polls=0):
 def set_lookback_jitter(seed=0):
     """Look-back stress switch (0 = off); see include/rlscan_debug.h."""
     _check("rlscan_debug_set_lookback_jitter", lib().rlscan_debug_set_lookback_jitter(int(seed)))
+
+
+def rlscan_debug_stream(inputs, outputs):
+    """Streaming reference (include/rlscan_debug.h): reads the float32 tensors
+    `inputs`, writes `outputs` (all the same number of elements, a multiple of
+    4096), with the scan kernels' access pattern and no scan."""
+    n = inputs[0].numel()
+    ins = (ctypes.c_void_p * len(inputs))(*[t.data_ptr() for t in inputs])
+    outs = (ctypes.c_void_p * len(outputs))(*[t.data_ptr() for t in outputs])
+    _check("rlscan_debug_stream", lib().rlscan_debug_stream(ins, len(inputs), outs, len(outputs), n,
+                                                            _stream(inputs[0].device)))
 
 
 def rlscan_debug_wave_scan(a, b, out_a, out_b):

@@ -239,6 +239,42 @@ def test_check_inputs_validation(L):
     assert b"workspace" in L.rlscan_last_error()
 
 
+def test_stream_reference_validation(L):
+    VP = ctypes.c_void_p
+    L.rlscan_debug_stream.argtypes = [ctypes.POINTER(VP), ctypes.c_int, ctypes.POINTER(VP),
+                                      ctypes.c_int, ctypes.c_int64, VP]
+    ins = (VP * 5)(*[0x100000 + 0x1000 * i for i in range(5)])
+    outs = (VP * 2)(0x200000, 0x300000)
+    assert L.rlscan_debug_stream(None, 5, outs, 2, 4096, N) == NULL_ARG
+    assert L.rlscan_debug_stream(ins, 5, None, 2, 4096, N) == NULL_ARG
+    assert L.rlscan_debug_stream(ins, 5, outs, 1, 4096, N) == BAD_PARAM   # (5, 1) not built
+    assert L.rlscan_debug_stream(ins, 0, outs, 1, 4096, N) == BAD_PARAM
+    assert L.rlscan_debug_stream(ins, 5, outs, 2, 4000, N) == BAD_SHAPE
+    assert L.rlscan_debug_stream(ins, 5, outs, 2, 0, N) == BAD_SHAPE
+    bad = (VP * 2)(0x200004, 0x300000)
+    assert L.rlscan_debug_stream(ins, 5, bad, 2, 4096, N) == BAD_PARAM   # misaligned
+    holes = (VP * 2)(0x200000, None)
+    assert L.rlscan_debug_stream(ins, 5, holes, 2, 4096, N) == NULL_ARG
+
+
+def test_phase_stamps_only_in_the_profiling_build(L):
+    L.rlscan_debug_set_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    assert L.rlscan_debug_phase_stamps_built() == 0
+    assert L.rlscan_debug_set_phase_stamps(ctypes.c_void_p(0x100000), 16) == BAD_PARAM
+    assert L.rlscan_debug_set_phase_stamps(None, 0) == OK
+    from linear_recurrence_scan_amd import build
+    if not os.path.exists(build.STAMPS_LIB):
+        pytest.skip("librlscan_stamps.so not built")
+    S = ops._declare(ctypes.CDLL(build.STAMPS_LIB))
+    assert S.rlscan_debug_phase_stamps_built() == 1
+    assert S.rlscan_debug_set_phase_stamps(ctypes.c_void_p(0x100004), 16) == BAD_PARAM  # alignment
+    assert S.rlscan_debug_set_phase_stamps(ctypes.c_void_p(0x100000), 0) == BAD_SHAPE
+    assert S.rlscan_debug_set_phase_stamps(ctypes.c_void_p(0x100000), 16) == OK
+    assert S.rlscan_debug_set_phase_stamps(None, 0) == OK
+    for name in declared_functions():
+        assert hasattr(S, name), f"profiling build misses {name}"
+
+
 def test_spin_limit_switch(L):
     L.rlscan_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
     assert L.rlscan_debug_set_spin_limit(5) == OK

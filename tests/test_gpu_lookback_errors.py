@@ -137,3 +137,18 @@ def test_shapes_without_look_back_run_without_a_workspace(E, T):
     for got, want in ((adv, want_adv), (ret, want_ret)):
         err = np.abs(host(got) - want) / np.maximum(1.0, np.abs(want))
         assert err.max() <= 1e-4
+
+
+@pytest.mark.parametrize("nin,nout", [(1, 1), (2, 1), (4, 2), (5, 2), (6, 2)])
+def test_stream_reference_kernel_writes_the_sum(nin, nout):
+    """The streaming reference the bench compares each scan with moves the
+    arrays it is given: every output is the elementwise sum of the inputs."""
+    n = 3 * 4096
+    g = torch.Generator().manual_seed(nin * 10 + nout)
+    ins = [torch.randn(n, generator=g).to("cuda") for _ in range(nin)]
+    outs = [torch.full((n,), float("nan"), device="cuda") for _ in range(nout)]
+    ops.rlscan_debug_stream(ins, outs)
+    want = sum(t.double() for t in ins)
+    for o in outs:
+        torch.cuda.synchronize()
+        assert torch.allclose(o.double(), want, rtol=1e-6, atol=1e-5)
