@@ -77,3 +77,29 @@ def test_summary_without_a_calibration_copy_writes_no_traffic(tmp_path):
                             str(out), "test")
     assert not (out / os.path.basename(bench.TRAFFIC_FILE)).exists()
     assert "HBM traffic" not in (out / "scan_kernels_bench_default_kernel_trace.md").read_text()
+
+
+def test_summary_tabulates_the_sq_counter_pass(tmp_path):
+    sq = tmp_path / "sq"
+    os.makedirs(sq)
+    with open(sq / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for did, val in ((1, 10.0), (2, 14.0), (3, 12.0)):
+            for name, v in (("VALUBusy", val), ("OccupancyPercent", 45.0), ("SQ_INSTS_VALU", 2220032.0),
+                            ("SQ_WAVES", 8192.0), ("MemUnitStalled", 0.5)):
+                w.writerow([did, GAE, name, v])
+        w.writerow([4, COPY, "VALUBusy", 1.0])  # not a library kernel: left out
+    write = [(1, 131072, COPY, 16384.0), (2, 524288, GAE, 32768.0)]
+    fetch = [(1, 131072, COPY, 8192.0), (2, 524288, GAE, 41000.0)]
+    _write_counters(str(tmp_path / "fetch"), "FETCH_SIZE", fetch)
+    _write_counters(str(tmp_path / "write"), "WRITE_SIZE", write)
+    _write_trace(str(tmp_path / "trace"))
+    out = tmp_path / "out"
+    bench.summarize_profile(str(tmp_path / "trace"), str(tmp_path / "fetch"), str(tmp_path / "write"),
+                            str(out), "test", str(sq))
+    text = (out / "scan_kernels_bench_default_kernel_trace.md").read_text()
+    assert "## SQ counters" in text
+    # 2,220,032 VALU instructions over 8192 waves = 271 per wave; median VALU busy 12.0
+    assert "| `scan_kernel<GaeOp<3u, false>, 8, 2, false>` | 3 | 271 | 12.0 | 45.0 | 0.50 |" in text
+    assert "copyBuffer" not in text.split("## SQ counters")[1]
