@@ -76,6 +76,9 @@ rlscan_status finish_plan(int64_t E, int64_t T, int tile, int waves, bool vec_ok
     plan.geo.vec_ok = vec_ok ? 1 : 0;
     plan.lookback = plan.geo.num_tiles > 1 && (tile % T) != 0;
     plan.geo.interleave = (plan.lookback && E > 1 && T % tile == 0) ? 1 : 0;
+    // column-major tiles: a tile's predecessors are E, 2E, ... block indices
+    // back, on its own XCD when E is a multiple of 8 (see lookback_poll_local)
+    plan.geo.xcd_local = (plan.geo.interleave && E % 8 == 0) ? 1 : 0;
     plan.geo.boost = 0;  // decided per kernel at launch
     plan.geo.jitter = g_jitter.load(std::memory_order_relaxed);
     plan.geo.spins = g_spins.load(std::memory_order_relaxed);

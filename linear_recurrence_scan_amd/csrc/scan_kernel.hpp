@@ -289,7 +289,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
             const uint64_t t = readfirstlane_u64(((uint64_t)thi << 32) | tlo);
             if (lane == 0) epoch_advance(ws, q, g.num_tiles, t);
             x = lookback(ws, (uint32_t)(t >> 32), q, stride, ttot, need_carry, early, g.jitter,
-                         g.spins);
+                         g.spins, g.xcd_local != 0);
         }
         if constexpr (WAVES > 1) {
             if (threadIdx.x == 0) sh.carry = x;

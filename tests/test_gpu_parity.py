@@ -822,6 +822,38 @@ def test_lookback_results_do_not_depend_on_timing(seed):
     assert ops.workspace_error() == 0
 
 
+@pytest.mark.parametrize("E", [8, 24, 64, 12])
+def test_lookback_polls_on_the_tiles_own_xcd(E):
+    """Rows of whole 4096-step tiles run column-major, so a tile's scan
+    predecessors are E, 2E, ... workgroups back: on its own XCD when E is a
+    multiple of 8, where the look-back polls through that XCD's L2 with
+    scalar loads (E = 12 takes the device-scope polls).  Backward and forward
+    scans against the oracle, and bitwise the same under scrambled
+    publication timing."""
+    T = 4096 * 6
+    d = synth.long_row_inputs(E=E, T=T, seed=E + 11)
+    args = (dev(d["rewards"]), dev(d["terminateds"]), dev(d["truncateds"]))
+    got = ops.discounted_returns(*args, 0.999, dev(d["bootstrap_values"]))
+    want = oracle.discounted_returns(d["rewards"], d["terminateds"], d["truncateds"], f32(0.999),
+                                     d["bootstrap_values"])
+    assert_close(got, want, T, f"discounted {E}x{T}")
+    f = synth.forward_inputs(E, T, seed=E + 12)
+    fwd = lambda: ops.eligibility_traces(dev(f["inputs"]), dev(f["dones"]), 0.99, 0.97,  # noqa: E731
+                                         dev(f["seed_values"]))
+    plain = fwd()
+    want = oracle.eligibility_traces(f["inputs"], f["dones"], 0.99, 0.97, f["seed_values"],
+                                     decay=f32(0.99 * 0.97))
+    assert_close(plain, want, T, f"traces {E}x{T}")
+    ops.set_lookback_jitter(0x5EED + E)
+    try:
+        np.testing.assert_array_equal(host(fwd()), host(plain))
+        again = ops.discounted_returns(*args, 0.999, dev(d["bootstrap_values"]))
+        np.testing.assert_array_equal(host(again), host(got))
+    finally:
+        ops.set_lookback_jitter(0)
+    assert ops.workspace_error() == 0
+
+
 # ---------------------------------------------------------------------------
 # row lengths around every tile size the planner uses
 # ---------------------------------------------------------------------------
