@@ -110,8 +110,13 @@ int device_cus() {
     return v - 1;
 }
 
-// Plans a launch of a 4-elements-per-lane kernel.
-rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
+// Plans a launch of a 4-elements-per-lane kernel.  `deep_tiles` false: the
+// op's four-segment kernel is slower than its 8-wave one wherever the rules
+// below pick 4096-element tiles of 4 waves x 4 segments, so it takes 8 waves x
+// 2 segments there instead (V-trace: its four-segment look-back kernel needs
+// 120 VGPRs; 4194 x 1000 took 26.2 us against 22.4, 1000 x 4100 26.0 against
+// 21.6, 2000 x 4500 42.9 against 41.5).
+rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok, bool deep_tiles) {
     const int64_t N = E * T;
     int tile = 0, waves = 0;
     if (T < 4) {
@@ -126,9 +131,23 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
         // per lane.
         //  - Tiny problems take small tiles so that more workgroups share the
         //    work.
-        //  - Rows of 4096 steps or longer take 4096-element tiles of 8 waves x
-        //    2 segments (whole rows per tile, or fewer look-back hops along a
-        //    long row).
+        //  - Rows longer than 4096 steps (fp32 GAE, V-trace, discounted
+        //    returns and prefix sums over 4 x 2M to 4096 x 8192 steps):
+        //    * rows that straddle tiles, fewer than 8 rows, or at most
+        //      one_round steps in all take 4096-element tiles of 4 waves x 4
+        //      segments (prefix sums 1000 x 4100: 12.7 us against 15.0 for
+        //      8 waves x 2; returns 64 x 65536: 16.2 against 18.2);
+        //    * rows of at most four 4096-element tiles keep 8 waves x 2
+        //      segments (returns 512 x 16384: 30.4 us, against 31.3-31.4 for
+        //      the others);
+        //    * longer rows of whole tiles take 2048-element tiles of 4 waves.
+        //      Their look-backs poll through the XCD's L2 (column-major tiles,
+        //      see lookback_poll_local), so twice the hops cost less than
+        //      what the smaller tiles gain: 64 x 131072 prefix sums took 22.9
+        //      us against 23.5 (8 waves x 2) and 24.5 (4 waves x 4), returns
+        //      31.5 against 32.1, fp32 GAE 42.7 against 43.1.
+        //  - Rows of exactly 4096 steps take 4096-element tiles of 8 waves x 2
+        //    segments (whole rows per tile).
         //  - Rows that divide 4096 need no look-back at any tile size.  A grid
         //    of one round (more than half of one_round, at most one_round)
         //    takes 4096-element tiles of 8 waves: fewer, larger workgroups
@@ -149,7 +168,19 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
         if (N <= (int64_t)256 * 1024) {
             tile = 256;
             waves = 1;
-        } else if (T >= 4096) {
+        } else if (T > 4096) {
+            const bool straddles = T % 4096 != 0;
+            if (straddles || E < 8 || N <= one_round) {
+                tile = 4096;
+                waves = 4;
+            } else if (T <= 4 * 4096) {
+                tile = 4096;
+                waves = 8;
+            } else {
+                tile = 2048;
+                waves = 4;
+            }
+        } else if (T == 4096) {
             tile = 4096;
             waves = 8;
         } else if (whole_rows && one_round > 0 &&
@@ -166,6 +197,7 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok) {
             tile = 2048;
             waves = 4;
         }
+        if (!deep_tiles && tile == 4096 && waves == 4) waves = 8;
     }
     return finish_plan(E, T, tile, waves, vec_ok, plan);
 }
@@ -277,7 +309,7 @@ rlscan_status gae_prepare(const float* rewards, const float* values, const float
     const bool vec = aligned16(rewards) && aligned16(values) && aligned16(terminateds) &&
                      aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(advantages) &&
                      aligned16(returns) && aligned16(skip);
-    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec, true));
     a = GaeArgs{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
                 advantages, returns, gamma, lambda, skip, nullptr};
     return RLSCAN_OK;
@@ -354,7 +386,7 @@ rlscan_status rlscan_gae_norm(const float* rewards, const float* values, const f
                      aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(advantages) &&
                      aligned16(returns);
     Plan plan;
-    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec, true));
     GaeArgs a{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
               advantages, returns, gamma, lambda, nullptr, nullptr};
     return launch_gae_norm(a, plan, ws, norm_stats_offset(num_envs, seq_len), num_envs * seq_len,
@@ -499,7 +531,7 @@ rlscan_status rlscan_gae_bf16(const uint16_t* rewards, const uint16_t* values,
     const bool vec = a8(rewards) && a8(values) && a4(terminateds) && a4(truncateds) &&
                      a8(bootstrap_values) && a8(advantages) && a8(returns);
     Plan plan;
-    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec, true));
     RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
     GaeCompactArgs a{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
                      advantages, returns, gamma, lambda};
@@ -558,7 +590,7 @@ rlscan_status rlscan_vtrace(const float* log_pi_target, const float* log_pi_beha
                      aligned16(rewards) && aligned16(terminateds) && aligned16(truncateds) &&
                      aligned16(bootstrap_values) && aligned16(vs) && aligned16(pg_advantages);
     Plan plan;
-    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec, false));
     RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
     VtraceArgs a{log_pi_target, log_pi_behavior, values, rewards, terminateds, truncateds,
                  bootstrap_values, last_value, vs, pg_advantages, gamma, rho_bar, c_bar};
@@ -610,7 +642,7 @@ rlscan_status rlscan_returns(const float* rewards, const float* next_values,
     const bool vec = aligned16(rewards) && aligned16(next_values) && aligned16(terminateds) &&
                      aligned16(truncateds) && aligned16(bootstrap_values) && aligned16(out);
     Plan plan;
-    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec, true));
     RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
     ReturnsArgs a{rewards, next_values, terminateds, truncateds, bootstrap_values, out, gamma, lambda};
     return launch_returns(a, plan, ws, reinterpret_cast<hipStream_t>(stream));
@@ -630,7 +662,7 @@ rlscan_status rlscan_prefix(const float* inputs, const float* dones, const float
     RLSCAN_REQUIRE(out, "out");
     const bool vec = aligned16(inputs) && aligned16(dones) && aligned16(out);
     Plan plan;
-    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec));
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec, true));
     RLSCAN_TRY(check_ws(plan, ws, ws_bytes));
     PrefixArgs a{inputs, dones, seed, out, decay, boundary == RLSCAN_STARTS_AT ? 1 : 0};
     return launch_prefix(a, plan, ws, reinterpret_cast<hipStream_t>(stream));

@@ -822,15 +822,25 @@ def test_lookback_results_do_not_depend_on_timing(seed):
     assert ops.workspace_error() == 0
 
 
+@pytest.mark.parametrize("shape", [(0, 0), (2048, 4), (4096, 8)], ids=["planner", "2048x4", "4096x8"])
 @pytest.mark.parametrize("E", [8, 24, 64, 12])
-def test_lookback_polls_on_the_tiles_own_xcd(E):
-    """Rows of whole 4096-step tiles run column-major, so a tile's scan
-    predecessors are E, 2E, ... workgroups back: on its own XCD when E is a
-    multiple of 8, where the look-back polls through that XCD's L2 with
-    scalar loads (E = 12 takes the device-scope polls).  Backward and forward
-    scans against the oracle, and bitwise the same under scrambled
-    publication timing."""
+def test_lookback_polls_on_the_tiles_own_xcd(E, shape):
+    """Rows of whole tiles run column-major, so a tile's scan predecessors are
+    E, 2E, ... workgroups back: on its own XCD when E is a multiple of 8,
+    where the look-back polls through that XCD's L2 with scalar loads (E = 12
+    takes the device-scope polls).  Backward and forward scans against the
+    oracle, and bitwise the same under scrambled publication timing, with the
+    planner's launch shape and with the two shapes long rows take at larger
+    sizes."""
     T = 4096 * 6
+    ops.set_launch_shape(*shape)
+    try:
+        _xcd_lookback_case(E, T)
+    finally:
+        ops.set_launch_shape(0, 0)
+
+
+def _xcd_lookback_case(E, T):
     d = synth.long_row_inputs(E=E, T=T, seed=E + 11)
     args = (dev(d["rewards"]), dev(d["terminateds"]), dev(d["truncateds"]))
     got = ops.discounted_returns(*args, 0.999, dev(d["bootstrap_values"]))
