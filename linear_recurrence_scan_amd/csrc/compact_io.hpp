@@ -16,9 +16,15 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two values rounded to bf16 (nearest, ties to even), `lo` in the low half:
+// one v_cvt_pk_bf16_f32 of both.  Converting each value on its own took four
+// instructions (two conversions, a shift and an or).
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // A lane's four consecutive bf16 values (8 bytes), widened, in scan order.
