@@ -102,6 +102,29 @@ __device__ __forceinline__ Affine wave_inclusive_scan(Affine x) {
     return Affine{a, b};
 }
 
+// Inclusive sum over the 64 lanes of a wave, by the same six steps and DPP
+// rules as wave_inclusive_scan (one v_add_f32_dpp each): lane l receives
+// x_0 + ... + x_l, so lane 63 holds the wave's total, summed in a fixed
+// order.  Must be called by all 64 lanes (full EXEC).
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:1 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:2 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:4 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_shr:8 row_mask:0xf bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_bcast:15 row_mask:0xa bank_mask:0xf\n\t"
+        "s_nop 1\n\t"
+        "v_add_f32_dpp %0, %0, %0 row_bcast:31 row_mask:0xc bank_mask:0xf\n\t"
+        "s_nop 1"
+        : "+v"(x));
+    return x;
+}
+
 // Value of lane l-1 for every lane l; lane 0 receives `lane0`.
 __device__ __forceinline__ float wave_shift_prev(float x, float lane0) {
     return dpp<kWaveShr1>(lane0, x);

@@ -336,24 +336,62 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
     }
     stamp(g, q, 5);
     if constexpr (kStats) {
-        // lanes: butterfly merges (a fixed pattern, so the result is
-        // reproducible); waves: merged in order by thread 0
+        if (FAST || tl.rem == (uint32_t)TILE) {
+            // A whole tile (also one with unaligned arrays, so that aligned
+            // and unaligned calls give the same bits): every lane holds
+            // SEGS*G outputs and every wave 64*SEGS*G, so each level's mean
+            // is the plain mean of the means below it, and its M2 their M2s
+            // plus the count times the squared distances to that mean (sums
+            // in a fixed order: reproducible).  No division, and no lane
+            // exchange beyond two DPP sums per wave.  The condition is
+            // uniform over the workgroup.
+            constexpr float kLane = (float)(SEGS * G), kWaveN = 64.f * kLane;
+            const float wm = readlane(wave_inclusive_sum(st.m), kWave - 1) * (1.f / 64.f);
+            const float dl = st.m - wm;
+            const float wm2 = readlane(wave_inclusive_sum(fmaf(dl * dl, kLane, st.m2)), kWave - 1);
+            st = Stat{kWaveN, wm, wm2};
+            if constexpr (WAVES > 1) {
+                if (lane == 0) {
+                    sh.st_m[wave] = st.m;
+                    sh.st_m2[wave] = st.m2;
+                }
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    float sm = 0.f;
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const Stat o{__shfl_xor(st.n, off), __shfl_xor(st.m, off), __shfl_xor(st.m2, off)};
-            st = stat_merge(st, o);
-        }
-        if constexpr (WAVES > 1) {
-            if (lane == 0) {
-                sh.st_n[wave] = st.n;
-                sh.st_m[wave] = st.m;
-                sh.st_m2[wave] = st.m2;
+                    for (int u = 0; u < WAVES; ++u) sm += sh.st_m[u];
+                    const float tm = sm * (1.f / (float)WAVES);
+                    float tm2 = 0.f;
+#pragma unroll
+                    for (int u = 0; u < WAVES; ++u) {
+                        const float d = sh.st_m[u] - tm;
+                        tm2 += fmaf(d * d, kWaveN, sh.st_m2[u]);
+                    }
+                    st = Stat{kWaveN * (float)WAVES, tm, tm2};
+                }
             }
-            __syncthreads();
-            if (threadIdx.x == 0) {
-                st = Stat{sh.st_n[0], sh.st_m[0], sh.st_m2[0]};
+        } else {
+            // The batch's last tile, partly past its end: lanes hold
+            // different counts.  Lanes: butterfly merges (a fixed pattern, so
+            // the result is reproducible); waves: merged in order by thread 0.
 #pragma unroll
-                for (int u = 1; u < WAVES; ++u) st = stat_merge(st, Stat{sh.st_n[u], sh.st_m[u], sh.st_m2[u]});
+            for (int off = 32; off >= 1; off >>= 1) {
+                const Stat o{__shfl_xor(st.n, off), __shfl_xor(st.m, off), __shfl_xor(st.m2, off)};
+                st = stat_merge(st, o);
+            }
+            if constexpr (WAVES > 1) {
+                if (lane == 0) {
+                    sh.st_n[wave] = st.n;
+                    sh.st_m[wave] = st.m;
+                    sh.st_m2[wave] = st.m2;
+                }
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    st = Stat{sh.st_n[0], sh.st_m[0], sh.st_m2[0]};
+#pragma unroll
+                    for (int u = 1; u < WAVES; ++u)
+                        st = stat_merge(st, Stat{sh.st_n[u], sh.st_m[u], sh.st_m2[u]});
+                }
             }
         }
         if (threadIdx.x == 0) {
