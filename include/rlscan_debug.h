@@ -32,6 +32,19 @@ rlscan_status rlscan_debug_wave_scan(const float* a, const float* b, float* out_
  * Errors: any other pair -> BAD_PARAM. */
 rlscan_status rlscan_debug_set_launch_shape(int tile, int waves);
 
+/* The launch shape, *tile elements per workgroup of *waves waves, that the
+ * planner picks for the scans with four elements per lane (GAE and its
+ * compact, skip-mask and normalising forms, returns, prefix sums; V-trace
+ * when `vtrace` is nonzero) over num_envs rows of seq_len steps, on a device
+ * of `compute_units` CUs (0: the current device's, read once per device).
+ * Rows of fewer than 4 steps report their own kernels' shape (2048, 4).
+ * rlscan_debug_set_launch_shape does not change the answer.  Host only: with
+ * compute_units > 0 it makes no HIP call.
+ * Errors: NULL tile or waves -> NULL_ARG; num_envs or seq_len < 1, or a shape
+ * the estimators reject -> BAD_SHAPE; compute_units < 0 -> BAD_PARAM. */
+rlscan_status rlscan_debug_g4_shape(int64_t num_envs, int64_t seq_len, int vtrace,
+                                    int compute_units, int* tile, int* waves);
+
 /* Look-back stress switch: with a nonzero `seed`, every later call whose rows
  * span tiles delays each tile by a bounded pseudo-random time (up to about
  * 6 microseconds, a function of the seed and the tile) before it publishes

@@ -110,14 +110,92 @@ int device_cus() {
     return v - 1;
 }
 
-// Plans a launch of a 4-elements-per-lane kernel.  `deep_tiles` false: the
-// op's four-segment kernel is slower than its 8-wave one wherever the rules
-// below pick 4096-element tiles of 4 waves x 4 segments, so it takes 8 waves x
-// 2 segments there instead (V-trace: its four-segment look-back kernel needs
+// The launch shape of a 4-elements-per-lane kernel for E rows of T >= 4 steps
+// on a device of `cus` compute units.  `deep_tiles` false: the op's
+// four-segment kernel is slower than its 8-wave one wherever the rules below
+// pick 4096-element tiles of 4 waves x 4 segments, so it takes 8 waves x 2
+// segments there instead (V-trace: its four-segment look-back kernel needs
 // 120 VGPRs; 4194 x 1000 took 26.2 us against 22.4, 1000 x 4100 26.0 against
 // 21.6, 2000 x 4500 42.9 against 41.5).
-rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok, bool deep_tiles) {
+void g4_shape(int64_t E, int64_t T, int64_t cus, bool deep_tiles, int& tile, int& waves) {
     const int64_t N = E * T;
+    // Measured on MI355X (fp32 GAE over 1M-67M steps, rows of 333 to 4096
+    // steps, every launch shape).  `one_round` is the number of steps the
+    // device holds at once: 8 waves on each of 4 SIMDs per CU, 8 steps
+    // per lane.
+    //  - Tiny problems take small tiles so that more workgroups share the
+    //    work.
+    //  - Rows longer than 4096 steps (fp32 GAE, V-trace, discounted
+    //    returns and prefix sums over 4 x 2M to 4096 x 8192 steps):
+    //    * rows that straddle tiles, fewer than 8 rows, or at most
+    //      one_round steps in all take 4096-element tiles of 4 waves x 4
+    //      segments (prefix sums 1000 x 4100: 12.7 us against 15.0 for
+    //      8 waves x 2; returns 64 x 65536: 16.2 against 18.2);
+    //    * rows of at most four 4096-element tiles keep 8 waves x 2
+    //      segments (returns 512 x 16384: 30.4 us, against 31.3-31.4 for
+    //      the others);
+    //    * longer rows of whole tiles take 2048-element tiles of 4 waves.
+    //      Their look-backs poll through the XCD's L2 (column-major tiles,
+    //      see lookback_poll_local), so twice the hops cost less than
+    //      what the smaller tiles gain: 64 x 131072 prefix sums took 22.9
+    //      us against 23.5 (8 waves x 2) and 24.5 (4 waves x 4), returns
+    //      31.5 against 32.1, fp32 GAE 42.7 against 43.1.
+    //  - Rows of exactly 4096 steps take 4096-element tiles of 8 waves x 2
+    //    segments (whole rows per tile).
+    //  - Rows that divide 4096 need no look-back at any tile size.  A grid
+    //    of one round (more than half of one_round, at most one_round)
+    //    takes 4096-element tiles of 8 waves: fewer, larger workgroups
+    //    were 0.3-2% faster at 4096 x 1024.  Otherwise small workgroups
+    //    refill freed slots sooner: 1024-element tiles of 2 waves (rows
+    //    that divide 1024), else 2048-element tiles of 4 waves.
+    //    Past four rounds the larger tiles win again: 4096-element tiles
+    //    of 8 waves took 168-169 us at 32768 x 1024 against 175.5 for
+    //    1024-element ones, and 338 against 343-345 us at 65536 x 1024
+    //    (between two and four rounds the shapes were within noise).
+    //  - Other rows straddle tiles, and each tile looks back to its
+    //    predecessor.  From 5/8 of one_round up, 4096-element tiles of 4
+    //    waves x 4 segments halve the look-backs of 2048-element tiles and
+    //    were 6-10% faster (4194 x 1000: 22.5 against 25.0 us); below it,
+    //    2048-element tiles of 4 waves.
+    const int64_t one_round = cus * 4 * 8 * 512;
+    const bool whole_rows = 4096 % T == 0;
+    if (N <= (int64_t)256 * 1024) {
+        tile = 256;
+        waves = 1;
+    } else if (T > 4096) {
+        const bool straddles = T % 4096 != 0;
+        if (straddles || E < 8 || N <= one_round) {
+            tile = 4096;
+            waves = 4;
+        } else if (T <= 4 * 4096) {
+            tile = 4096;
+            waves = 8;
+        } else {
+            tile = 2048;
+            waves = 4;
+        }
+    } else if (T == 4096) {
+        tile = 4096;
+        waves = 8;
+    } else if (whole_rows && one_round > 0 &&
+               ((2 * N > one_round && N <= one_round) || N > 4 * one_round)) {
+        tile = 4096;
+        waves = 8;
+    } else if (1024 % T == 0) {
+        tile = 1024;
+        waves = 2;
+    } else if (!whole_rows && one_round > 0 && 8 * N >= 5 * one_round) {
+        tile = 4096;
+        waves = 4;
+    } else {
+        tile = 2048;
+        waves = 4;
+    }
+    if (!deep_tiles && tile == 4096 && waves == 4) waves = 8;
+}
+
+// Plans a launch of a 4-elements-per-lane kernel (see g4_shape).
+rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok, bool deep_tiles) {
     int tile = 0, waves = 0;
     if (T < 4) {
         // rows shorter than a lane's four-element group have kernels of their
@@ -125,79 +203,7 @@ rlscan_status plan_g4(int64_t E, int64_t T, Plan& plan, bool vec_ok, bool deep_t
         tile = kShortRowTile;
         waves = kShortRowWaves;
     } else if (!cfg_override(tile, waves)) {
-        // Measured on MI355X (fp32 GAE over 1M-67M steps, rows of 333 to 4096
-        // steps, every launch shape).  `one_round` is the number of steps the
-        // device holds at once: 8 waves on each of 4 SIMDs per CU, 8 steps
-        // per lane.
-        //  - Tiny problems take small tiles so that more workgroups share the
-        //    work.
-        //  - Rows longer than 4096 steps (fp32 GAE, V-trace, discounted
-        //    returns and prefix sums over 4 x 2M to 4096 x 8192 steps):
-        //    * rows that straddle tiles, fewer than 8 rows, or at most
-        //      one_round steps in all take 4096-element tiles of 4 waves x 4
-        //      segments (prefix sums 1000 x 4100: 12.7 us against 15.0 for
-        //      8 waves x 2; returns 64 x 65536: 16.2 against 18.2);
-        //    * rows of at most four 4096-element tiles keep 8 waves x 2
-        //      segments (returns 512 x 16384: 30.4 us, against 31.3-31.4 for
-        //      the others);
-        //    * longer rows of whole tiles take 2048-element tiles of 4 waves.
-        //      Their look-backs poll through the XCD's L2 (column-major tiles,
-        //      see lookback_poll_local), so twice the hops cost less than
-        //      what the smaller tiles gain: 64 x 131072 prefix sums took 22.9
-        //      us against 23.5 (8 waves x 2) and 24.5 (4 waves x 4), returns
-        //      31.5 against 32.1, fp32 GAE 42.7 against 43.1.
-        //  - Rows of exactly 4096 steps take 4096-element tiles of 8 waves x 2
-        //    segments (whole rows per tile).
-        //  - Rows that divide 4096 need no look-back at any tile size.  A grid
-        //    of one round (more than half of one_round, at most one_round)
-        //    takes 4096-element tiles of 8 waves: fewer, larger workgroups
-        //    were 0.3-2% faster at 4096 x 1024.  Otherwise small workgroups
-        //    refill freed slots sooner: 1024-element tiles of 2 waves (rows
-        //    that divide 1024), else 2048-element tiles of 4 waves.
-        //    Past four rounds the larger tiles win again: 4096-element tiles
-        //    of 8 waves took 168-169 us at 32768 x 1024 against 175.5 for
-        //    1024-element ones, and 338 against 343-345 us at 65536 x 1024
-        //    (between two and four rounds the shapes were within noise).
-        //  - Other rows straddle tiles, and each tile looks back to its
-        //    predecessor.  From 5/8 of one_round up, 4096-element tiles of 4
-        //    waves x 4 segments halve the look-backs of 2048-element tiles and
-        //    were 6-10% faster (4194 x 1000: 22.5 against 25.0 us); below it,
-        //    2048-element tiles of 4 waves.
-        const int64_t one_round = (int64_t)device_cus() * 4 * 8 * 512;
-        const bool whole_rows = 4096 % T == 0;
-        if (N <= (int64_t)256 * 1024) {
-            tile = 256;
-            waves = 1;
-        } else if (T > 4096) {
-            const bool straddles = T % 4096 != 0;
-            if (straddles || E < 8 || N <= one_round) {
-                tile = 4096;
-                waves = 4;
-            } else if (T <= 4 * 4096) {
-                tile = 4096;
-                waves = 8;
-            } else {
-                tile = 2048;
-                waves = 4;
-            }
-        } else if (T == 4096) {
-            tile = 4096;
-            waves = 8;
-        } else if (whole_rows && one_round > 0 &&
-                   ((2 * N > one_round && N <= one_round) || N > 4 * one_round)) {
-            tile = 4096;
-            waves = 8;
-        } else if (1024 % T == 0) {
-            tile = 1024;
-            waves = 2;
-        } else if (!whole_rows && one_round > 0 && 8 * N >= 5 * one_round) {
-            tile = 4096;
-            waves = 4;
-        } else {
-            tile = 2048;
-            waves = 4;
-        }
-        if (!deep_tiles && tile == 4096 && waves == 4) waves = 8;
+        g4_shape(E, T, device_cus(), deep_tiles, tile, waves);
     }
     return finish_plan(E, T, tile, waves, vec_ok, plan);
 }
@@ -705,6 +711,21 @@ rlscan_status rlscan_debug_set_launch_shape(int tile, int waves) {
     if (!known_shape(tile, waves))
         return set_error(RLSCAN_ERR_BAD_PARAM, "unknown launch shape (see rlscan_debug.h)");
     g_shape.store(tile << 4 | waves, std::memory_order_relaxed);
+    return RLSCAN_OK;
+}
+
+rlscan_status rlscan_debug_g4_shape(int64_t num_envs, int64_t seq_len, int vtrace,
+                                    int compute_units, int* tile, int* waves) {
+    if (!tile || !waves) return set_error(RLSCAN_ERR_NULL_ARG, "tile and waves must not be NULL");
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (empty_batch(num_envs, seq_len))
+        return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs and seq_len must be positive");
+    if (compute_units < 0) return set_error(RLSCAN_ERR_BAD_PARAM, "compute_units must be >= 0");
+    int t = kShortRowTile, w = kShortRowWaves;
+    if (seq_len >= 4)
+        g4_shape(num_envs, seq_len, compute_units > 0 ? compute_units : device_cus(), vtrace == 0, t, w);
+    *tile = t;
+    *waves = w;
     return RLSCAN_OK;
 }
 

@@ -98,6 +98,8 @@ def _declare(L):
     L.rlscan_prefix.argtypes = [vp] * 4 + [i64, i64, f32, ctypes.c_int, vp, sz, vp]
     L.rlscan_debug_wave_scan.argtypes = [vp, vp, vp, vp, ctypes.c_int, vp]
     L.rlscan_debug_set_launch_shape.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.rlscan_debug_g4_shape.argtypes = [i64, i64, ctypes.c_int, ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     L.rlscan_debug_set_lookback_jitter.argtypes = [ctypes.c_uint32]
     L.rlscan_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
     L.rlscan_debug_set_phase_stamps.argtypes = [vp, i64]
@@ -109,7 +111,7 @@ def _declare(L):
     for name in ("rlscan_debug_wave_scan", "rlscan_workspace_init", "rlscan_workspace_error",
                  "rlscan_gae_norm", "rlscan_traces_vec", "rlscan_gae", "rlscan_gae_noalloc",
                  "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
-                 "rlscan_check_inputs", "rlscan_debug_set_launch_shape",
+                 "rlscan_check_inputs", "rlscan_debug_set_launch_shape", "rlscan_debug_g4_shape",
                  "rlscan_debug_set_lookback_jitter", "rlscan_debug_set_spin_limit",
                  "rlscan_debug_stream", "rlscan_debug_set_phase_stamps"):
         getattr(L, name).restype = st
@@ -390,6 +392,17 @@ def set_launch_shape(tile=0, waves=0):
     """Forces the launch shape of the four-elements-per-lane scans ((0, 0):
     the planner's choice); see include/rlscan_debug.h."""
     _check("rlscan_debug_set_launch_shape", lib().rlscan_debug_set_launch_shape(int(tile), int(waves)))
+
+
+def planned_shape(num_envs, seq_len, vtrace=False, compute_units=0):
+    """(tile, waves) the planner picks for the four-elements-per-lane scans
+    over num_envs x seq_len (V-trace's choice with vtrace=True) on a device of
+    `compute_units` CUs (0: the current device's); see include/rlscan_debug.h."""
+    t, w = ctypes.c_int(0), ctypes.c_int(0)
+    _check("rlscan_debug_g4_shape",
+           lib().rlscan_debug_g4_shape(int(num_envs), int(seq_len), 1 if vtrace else 0,
+                                       int(compute_units), ctypes.byref(t), ctypes.byref(w)))
+    return t.value, w.value
 
 
 def set_spin_limit(polls=0):

@@ -289,6 +289,58 @@ def test_launch_shape_override_validation(L):
     assert L.rlscan_debug_set_launch_shape(0, 0) == OK
 
 
+# The planner's launch shapes on a 256-CU device (one round = 4,194,304 steps):
+# (num_envs, seq_len) -> (tile, waves) for the ops and for V-trace.
+PLANNER_TABLE = [
+    ((8, 128), (256, 1), (256, 1)),          # at most 256K steps: one-wave tiles
+    ((1, 3), (2048, 4), (2048, 4)),          # rows under 4 steps: their own kernels
+    ((100000, 2), (2048, 4), (2048, 4)),
+    ((4096, 1024), (4096, 8), (4096, 8)),    # whole rows, one round
+    ((3072, 1024), (4096, 8), (4096, 8)),
+    ((2048, 1024), (1024, 2), (1024, 2)),    # whole rows, half a round or less
+    ((8192, 1024), (1024, 2), (1024, 2)),    # two to four rounds
+    ((32768, 1024), (4096, 8), (4096, 8)),   # past four rounds
+    ((2097, 1000), (2048, 4), (2048, 4)),    # straddling rows below 5/8 of a round
+    ((4194, 1000), (4096, 4), (4096, 8)),    # ... from 5/8 of a round (V-trace: 8 waves)
+    ((1024, 4096), (4096, 8), (4096, 8)),    # rows of exactly one tile
+    ((1000, 4100), (4096, 4), (4096, 8)),    # long rows straddling tiles
+    ((1, 1000000), (4096, 4), (4096, 8)),
+    ((4, 2097152), (4096, 4), (4096, 8)),    # long rows, fewer than 8 of them
+    ((64, 65536), (4096, 4), (4096, 8)),     # long rows, at most one round
+    ((512, 16384), (4096, 8), (4096, 8)),    # rows of at most four tiles
+    ((1024, 8192), (4096, 8), (4096, 8)),
+    ((64, 131072), (2048, 4), (2048, 4)),    # longer rows of whole tiles
+    ((16, 524288), (2048, 4), (2048, 4)),
+]
+
+
+@pytest.mark.parametrize("shape,want,want_vtrace", PLANNER_TABLE)
+def test_planner_launch_shapes(L, shape, want, want_vtrace):
+    assert ops.planned_shape(*shape, compute_units=256) == want
+    assert ops.planned_shape(*shape, vtrace=True, compute_units=256) == want_vtrace
+
+
+def test_planner_shape_ignores_the_override(L):
+    ops.set_launch_shape(1024, 2)
+    try:
+        assert ops.planned_shape(64, 131072, compute_units=256) == (2048, 4)
+    finally:
+        ops.set_launch_shape(0, 0)
+
+
+def test_planner_shape_validation(L):
+    t, w = ctypes.c_int(0), ctypes.c_int(0)
+    assert L.rlscan_debug_g4_shape(4, 8, 0, 256, None, ctypes.byref(w)) == NULL_ARG
+    assert L.rlscan_debug_g4_shape(4, 8, 0, 256, ctypes.byref(t), None) == NULL_ARG
+    assert L.rlscan_debug_g4_shape(0, 8, 0, 256, ctypes.byref(t), ctypes.byref(w)) == BAD_SHAPE
+    assert L.rlscan_debug_g4_shape(4, 0, 0, 256, ctypes.byref(t), ctypes.byref(w)) == BAD_SHAPE
+    assert L.rlscan_debug_g4_shape(-1, 8, 0, 256, ctypes.byref(t), ctypes.byref(w)) == BAD_SHAPE
+    assert L.rlscan_debug_g4_shape(4, 1 << 31, 0, 256, ctypes.byref(t), ctypes.byref(w)) == BAD_SHAPE
+    assert L.rlscan_debug_g4_shape(4, 8, 0, -1, ctypes.byref(t), ctypes.byref(w)) == BAD_PARAM
+    assert L.rlscan_debug_g4_shape(4, 8, 0, 256, ctypes.byref(t), ctypes.byref(w)) == OK
+    assert (t.value, w.value) == (256, 1)
+
+
 def test_workspace_init_validation(L):
     assert L.rlscan_workspace_init(N, 4096, N) == NULL_ARG
     assert L.rlscan_workspace_init(ctypes.c_void_p(0x1010), 4096, N) == WORKSPACE
