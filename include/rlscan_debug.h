@@ -85,6 +85,17 @@ rlscan_status rlscan_debug_stream(const float* const* inputs, int num_inputs,
 int rlscan_debug_phase_stamps_built(void);
 rlscan_status rlscan_debug_set_phase_stamps(uint64_t* stamps, int64_t max_tiles);
 
+/* How the look-back of the flat scans reads its predecessors' partial
+ * results, for every later call in the process.  0 (the default): when a
+ * tile's predecessors ran on its own XCD (rows of whole tiles in
+ * column-major order, a row count that is a multiple of 8), it polls them
+ * with scalar loads served by that XCD's L2; otherwise it reads a window of
+ * 64 predecessors with device-scope loads.  1: always the device-scope
+ * window.  Results are the same bits either way; the switch exists to compare
+ * the two.  Process-wide; set it while no other thread is calling the
+ * library.  Errors: any other mode -> BAD_PARAM. */
+rlscan_status rlscan_debug_set_lookback_polls(int mode);
+
 /* Bound of every look-back wait, in polls, for every later call in the
  * process; 0 restores the default (about a second of waiting).  A wait that
  * reaches the bound gives up: the tile takes a NaN carry, so its outputs and

@@ -27,6 +27,7 @@ bool known_shape(int t, int w) {
 
 std::atomic<uint32_t> g_jitter{0};  // look-back stress delay seed (0 = off)
 std::atomic<uint32_t> g_spins{kSpinLimit};  // polls before a look-back wait gives up
+std::atomic<int> g_device_polls{0};  // 1: look-back polls through the device-scope window only
 std::atomic<uint64_t*> g_stamps{nullptr};    // phase-stamp buffer (profiling builds)
 std::atomic<int64_t> g_stamp_tiles{0};
 std::atomic<int> g_shape{-1};  // tile << 4 | waves; -1 = not read from the environment yet
@@ -78,7 +79,8 @@ rlscan_status finish_plan(int64_t E, int64_t T, int tile, int waves, bool vec_ok
     plan.geo.interleave = (plan.lookback && E > 1 && T % tile == 0) ? 1 : 0;
     // column-major tiles: a tile's predecessors are E, 2E, ... block indices
     // back, on its own XCD when E is a multiple of 8 (see lookback_poll_local)
-    plan.geo.xcd_local = (plan.geo.interleave && E % 8 == 0) ? 1 : 0;
+    plan.geo.xcd_local =
+        (plan.geo.interleave && E % 8 == 0 && g_device_polls.load(std::memory_order_relaxed) == 0) ? 1 : 0;
     plan.geo.boost = 0;  // decided per kernel at launch
     plan.geo.jitter = g_jitter.load(std::memory_order_relaxed);
     plan.geo.spins = g_spins.load(std::memory_order_relaxed);
@@ -695,6 +697,12 @@ rlscan_status rlscan_debug_set_phase_stamps(uint64_t* stamps, int64_t max_tiles)
         return set_error(RLSCAN_ERR_BAD_PARAM, "stamps must be 8-byte aligned");
     g_stamps.store(stamps, std::memory_order_relaxed);
     g_stamp_tiles.store(stamps ? max_tiles : 0, std::memory_order_relaxed);
+    return RLSCAN_OK;
+}
+
+rlscan_status rlscan_debug_set_lookback_polls(int mode) {
+    if (mode != 0 && mode != 1) return set_error(RLSCAN_ERR_BAD_PARAM, "lookback poll mode must be 0 or 1");
+    g_device_polls.store(mode, std::memory_order_relaxed);
     return RLSCAN_OK;
 }
 

@@ -102,6 +102,7 @@ def _declare(L):
                                         ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     L.rlscan_debug_set_lookback_jitter.argtypes = [ctypes.c_uint32]
     L.rlscan_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
+    L.rlscan_debug_set_lookback_polls.argtypes = [ctypes.c_int]
     L.rlscan_debug_set_phase_stamps.argtypes = [vp, i64]
     L.rlscan_debug_phase_stamps_built.restype = ctypes.c_int
     L.rlscan_debug_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
@@ -113,6 +114,7 @@ def _declare(L):
                  "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
                  "rlscan_check_inputs", "rlscan_debug_set_launch_shape", "rlscan_debug_g4_shape",
                  "rlscan_debug_set_lookback_jitter", "rlscan_debug_set_spin_limit",
+                 "rlscan_debug_set_lookback_polls",
                  "rlscan_debug_stream", "rlscan_debug_set_phase_stamps"):
         getattr(L, name).restype = st
     return L
@@ -403,6 +405,12 @@ def planned_shape(num_envs, seq_len, vtrace=False, compute_units=0):
            lib().rlscan_debug_g4_shape(int(num_envs), int(seq_len), 1 if vtrace else 0,
                                        int(compute_units), ctypes.byref(t), ctypes.byref(w)))
     return t.value, w.value
+
+
+def set_lookback_polls(mode=0):
+    """0: look-back polls through the XCD's L2 where the layout allows (the
+    default); 1: the device-scope window only; see include/rlscan_debug.h."""
+    _check("rlscan_debug_set_lookback_polls", lib().rlscan_debug_set_lookback_polls(int(mode)))
 
 
 def set_spin_limit(polls=0):

@@ -281,6 +281,13 @@ def test_spin_limit_switch(L):
     assert L.rlscan_debug_set_spin_limit(0) == OK   # back to the default bound
 
 
+def test_lookback_poll_switch_validation(L):
+    assert L.rlscan_debug_set_lookback_polls(2) == BAD_PARAM
+    assert L.rlscan_debug_set_lookback_polls(-1) == BAD_PARAM
+    assert L.rlscan_debug_set_lookback_polls(1) == OK
+    assert L.rlscan_debug_set_lookback_polls(0) == OK
+
+
 def test_launch_shape_override_validation(L):
     assert L.rlscan_debug_set_launch_shape(1024, 3) == BAD_PARAM
     assert L.rlscan_debug_set_launch_shape(512, 1) == BAD_PARAM

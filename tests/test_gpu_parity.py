@@ -829,9 +829,9 @@ def test_lookback_polls_on_the_tiles_own_xcd(E, shape):
     E, 2E, ... workgroups back: on its own XCD when E is a multiple of 8,
     where the look-back polls through that XCD's L2 with scalar loads (E = 12
     takes the device-scope polls).  Backward and forward scans against the
-    oracle, and bitwise the same under scrambled publication timing, with the
-    planner's launch shape and with the two shapes long rows take at larger
-    sizes."""
+    oracle, and bitwise the same under scrambled publication timing and with
+    the device-scope window instead of the L2 polls, with the planner's launch
+    shape and with the two shapes long rows take at larger sizes."""
     T = 4096 * 6
     ops.set_launch_shape(*shape)
     try:
@@ -861,6 +861,14 @@ def _xcd_lookback_case(E, T):
         np.testing.assert_array_equal(host(again), host(got))
     finally:
         ops.set_lookback_jitter(0)
+    # the device-scope window instead of the L2 polls: the same bits
+    ops.set_lookback_polls(1)
+    try:
+        np.testing.assert_array_equal(host(fwd()), host(plain))
+        again = ops.discounted_returns(*args, 0.999, dev(d["bootstrap_values"]))
+        np.testing.assert_array_equal(host(again), host(got))
+    finally:
+        ops.set_lookback_polls(0)
     assert ops.workspace_error() == 0
 
 
