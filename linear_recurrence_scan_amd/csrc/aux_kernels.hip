@@ -66,7 +66,8 @@ struct StreamPtrs {
 
 template <int NIN, int NOUT>
 __global__ __launch_bounds__(512) void stream_kernel(StreamPtrs p) {
-    const size_t base = (size_t)blockIdx.x * kStreamTile + threadIdx.x * 4;  // segment 0
+    const size_t t0 = (size_t)blockIdx.x * kStreamTile;
+    const size_t base = t0 + threadIdx.x * 4;  // segment 0
     f32x4 v[2][NIN];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -80,7 +81,9 @@ __global__ __launch_bounds__(512) void stream_kernel(StreamPtrs p) {
 #pragma unroll
         for (int a = 1; a < NIN; ++a) acc += v[s][a];
 #pragma unroll
-        for (int o = 0; o < NOUT; ++o) store16(p.out[o] + base + s * (kStreamTile / 2), acc);
+        for (int o = 0; o < NOUT; ++o)
+            store16<true>(p.out[o] + t0, (uint32_t)(threadIdx.x * 4 + s * (kStreamTile / 2)) * 4u,
+                          kStreamTile * 4u, acc);
     }
 }
 

@@ -28,6 +28,7 @@ struct GaeOp {
     static constexpr bool kFits64 = !kStats;
     GaeArgs p;
     __device__ double* stats_out() const { return p.tile_stats; }
+    __host__ __device__ int output_arrays() const { return p.returns ? 2 : 1; }
     struct Raw {
         float R[G], V[G], TE[G], TR[G], B[G];  // B: full bootstrap array (kBoot2D)
         float SK[G];                           // skip mask (kSkip)
@@ -92,15 +93,15 @@ struct GaeOp {
         }
     }
 
-    template <bool FAST>
+    template <bool FAST, bool SC1 = false>
     __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
                              const float (&)[G], const float (&)[G], const Keep (&kp)[G]) const {
-        store_group<G, true, FAST>(p.advantages + tl.lo, gr, A);
+        store_group<G, true, FAST, SC1>(p.advantages + tl.lo, gr, A);
         if (p.returns) {
             float R[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) R[j] = A[j] + kp[j].v;
-            store_group<G, true, FAST>(p.returns + tl.lo, gr, R);
+            store_group<G, true, FAST, SC1>(p.returns + tl.lo, gr, R);
         }
     }
 };

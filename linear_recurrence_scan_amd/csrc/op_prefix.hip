@@ -15,6 +15,7 @@ struct PrefixOp {
     static constexpr bool kEdgesAtLoad = true;
     static constexpr bool kFits64 = true;
     PrefixArgs p;
+    __host__ __device__ int output_arrays() const { return 1; }
     struct Raw {
         float X[G], D[G], S[G];
         float halo;
@@ -63,10 +64,10 @@ struct PrefixOp {
         }
     }
 
-    template <bool FAST>
+    template <bool FAST, bool SC1 = false>
     __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
                              const float (&)[G], const float (&)[G], const Keep (&)[G]) const {
-        store_group<G, false, FAST>(p.out + tl.lo, gr, A);
+        store_group<G, false, FAST, SC1>(p.out + tl.lo, gr, A);
     }
 };
 

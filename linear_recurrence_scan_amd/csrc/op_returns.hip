@@ -19,6 +19,7 @@ struct ReturnsOp {
     static constexpr bool kEdgesAtLoad = (F & kTrunc) == 0;
     static constexpr bool kFits64 = true;
     ReturnsArgs p;
+    __host__ __device__ int output_arrays() const { return 1; }
     struct Raw {
         float R[G], TE[G], TR[G], B[G], NV[G];
         EdgeValue<G, true, SHORT> eb;  // row-end carry bootstrap_values[:, T-1] without truncations
@@ -71,10 +72,10 @@ struct ReturnsOp {
         }
     }
 
-    template <bool FAST>
+    template <bool FAST, bool SC1 = false>
     __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
                              const float (&)[G], const float (&)[G], const Keep (&)[G]) const {
-        store_group<G, true, FAST>(p.out + tl.lo, gr, A);
+        store_group<G, true, FAST, SC1>(p.out + tl.lo, gr, A);
     }
 };
 

@@ -43,6 +43,7 @@ struct VtraceOp {
     static constexpr bool kEdgesAtLoad = (F & kBoot2D) == 0;
     static constexpr bool kFits64 = false;
     VtraceArgs p;
+    __host__ __device__ int output_arrays() const { return p.pg_advantages ? 2 : 1; }
     struct Raw {
         float LP[G], LB[G], R[G], V[G], TE[G], TR[G], B[G];  // B: full bootstrap array (kBoot2D)
         float halo;
@@ -106,14 +107,14 @@ struct VtraceOp {
         }
     }
 
-    template <bool FAST>
+    template <bool FAST, bool SC1 = false>
     __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G],
                              const float (&prevA)[G], const float (&al)[G],
                              const float (&be)[G], const Keep (&kp)[G]) const {
         float VS[G];
 #pragma unroll
         for (int j = 0; j < G; ++j) VS[j] = A[j] + kp[j].v;
-        store_group<G, true, FAST>(p.vs + tl.lo, gr, VS);
+        store_group<G, true, FAST, SC1>(p.vs + tl.lo, gr, VS);
         if (p.pg_advantages) {
             float PG[G];
 #pragma unroll
@@ -125,7 +126,7 @@ struct VtraceOp {
                     k = kp[j].k;
                 PG[j] = fmaf(k, prevA[j], al[j]);
             }
-            store_group<G, true, FAST>(p.pg_advantages + tl.lo, gr, PG);
+            store_group<G, true, FAST, SC1>(p.pg_advantages + tl.lo, gr, PG);
         }
     }
 };

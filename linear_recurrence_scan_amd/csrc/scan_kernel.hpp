@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "rlscan_internal.hpp"
 #include "scan_core.hpp"
@@ -147,7 +148,24 @@ struct WantsStats<Op, std::void_t<decltype(Op::kStats)>> {
     static constexpr bool value = Op::kStats;
 };
 
-template <class Op, int WAVES, int SEGS, bool LOOKBACK, bool FAST>
+// Ops that write their outputs through store_group declare output_arrays()
+// and take the store policy as their epilogue's second template argument;
+// the others store otherwise, and the policy does not apply to them.
+template <class Op, class = void>
+struct HasOutputArrays : std::false_type {};
+template <class Op>
+struct HasOutputArrays<Op, std::void_t<decltype(std::declval<const Op&>().output_arrays())>>
+    : std::true_type {};
+
+template <bool FAST, bool SC1, class Op, class... Args>
+__device__ __forceinline__ void run_epilogue(const Op& op, const Args&... args) {
+    if constexpr (HasOutputArrays<Op>::value)
+        op.template epilogue<FAST, SC1>(args...);
+    else
+        op.template epilogue<FAST>(args...);
+}
+
+template <class Op, int WAVES, int SEGS, bool LOOKBACK, bool FAST, bool SC1>
 __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile& tl, uint8_t* ws,
                                           int64_t q, int64_t stride, uint64_t ticket,
                                           TileShared& sh, float* lds_wave) {
@@ -316,7 +334,7 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
             A[j] = fmaf(be[s][j], y, al[s][j]);
             y = A[j];
         }
-        op.template epilogue<FAST>(tl, gr, A, prevA, al[s], be[s], kp[s]);
+        run_epilogue<FAST, SC1>(op, tl, gr, A, prevA, al[s], be[s], kp[s]);
         xs = fmaf(segtot[s].b, xs, segtot[s].a);
         if constexpr (kStats) {  // this group's valid outputs, merged into the lane's
             float n = 0.f, sum = 0.f;
@@ -412,7 +430,7 @@ struct WavesPerEu {
     static constexpr int value = (Op::kFits64 && !LOOKBACK && SEGS * Op::G <= 8) ? 8 : 1;
 };
 
-template <class Op, int WAVES, int SEGS, bool LOOKBACK>
+template <class Op, int WAVES, int SEGS, bool LOOKBACK, bool SC1>
 __global__ __launch_bounds__(WAVES * kWave)
 __attribute__((amdgpu_waves_per_eu(WavesPerEu<Op, SEGS, LOOKBACK>::value))) void scan_kernel(
     Op op, Geo g, uint8_t* ws) {
@@ -454,20 +472,47 @@ __attribute__((amdgpu_waves_per_eu(WavesPerEu<Op, SEGS, LOOKBACK>::value))) void
     tl.elems = TILE;
     const bool fast = g.vec_ok && rem >= TILE;
     if (fast)
-        scan_tile<Op, WAVES, SEGS, LOOKBACK, true>(op, g, tl, ws, q, stride, ticket, sh, lds_wave);
+        scan_tile<Op, WAVES, SEGS, LOOKBACK, true, SC1>(op, g, tl, ws, q, stride, ticket, sh, lds_wave);
     else
-        scan_tile<Op, WAVES, SEGS, LOOKBACK, false>(op, g, tl, ws, q, stride, ticket, sh, lds_wave);
+        scan_tile<Op, WAVES, SEGS, LOOKBACK, false, SC1>(op, g, tl, ws, q, stride, ticket, sh, lds_wave);
 }
 
 // Workgroups of `kernel` (no dynamic LDS) that one device holds at once:
 // occupancy per CU times the CU count, cached per kernel and device.
 int resident_workgroups(const void* kernel, int threads);
 
+// Whether a launch stores its full tiles' outputs with device scope
+// (store16).  Measured on MI355X, same-box A/B runs of the whole library:
+//  - two output arrays (GAE with returns, V-trace): unless the grid fills at
+//    most half of one round.  4096 x 1024 GAE 19.8 -> 19.4 us, V-trace
+//    19.1 -> 18.6, 8192 x 1024 GAE 40.7 -> 38.9, 17000 x 1024 GAE
+//    81.7 -> 78.8, 64 x 131072 GAE 42.8 -> 41.9 and V-trace 38.2 -> 36.8;
+//    2048 x 1024 GAE 11.5 -> 11.75 (half a round);
+//  - one output array (returns, prefix sums, GAE without returns): when the
+//    grid runs more than one round or its rows straddle tiles, but not for
+//    column-major long rows.  8192 x 1024 returns 28.3 -> 27.3 us and
+//    prefix sums 18.6 -> 18.0, 1000 x 4100 prefix sums 12.7 -> 11.9; a
+//    one-round 4096 x 1024 grid went 14.5 -> 14.8 (returns), and
+//    64 x 131072 returns 30.9 -> 31.9.
+inline bool sc1_stores(int outputs, const Geo& g, int64_t resident, bool lookback) {
+    if (outputs >= 2) return 2 * g.num_tiles > resident;
+    if (outputs == 1) return !g.interleave && (g.num_tiles > resident || lookback);
+    return false;
+}
+
 template <class Op, int WAVES, int SEGS, bool LOOKBACK>
 rlscan_status launch_one(const Op& op, Geo g, void* ws, size_t lds_bytes, hipStream_t stream) {
-    const void* k = reinterpret_cast<const void*>(&scan_kernel<Op, WAVES, SEGS, LOOKBACK>);
-    g.boost = (lds_bytes == 0 && g.num_tiles <= resident_workgroups(k, WAVES * kWave)) ? 1 : 0;
-    hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, LOOKBACK>), dim3((unsigned)g.num_tiles),
+    const void* k = reinterpret_cast<const void*>(&scan_kernel<Op, WAVES, SEGS, LOOKBACK, false>);
+    const int resident = resident_workgroups(k, WAVES * kWave);
+    g.boost = (lds_bytes == 0 && g.num_tiles <= resident) ? 1 : 0;
+    if constexpr (HasOutputArrays<Op>::value) {
+        if (sc1_stores(op.output_arrays(), g, resident, LOOKBACK)) {
+            hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, LOOKBACK, true>), dim3((unsigned)g.num_tiles),
+                               dim3(WAVES * kWave), lds_bytes, stream, op, g, static_cast<uint8_t*>(ws));
+            return RLSCAN_OK;
+        }
+    }
+    hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, LOOKBACK, false>), dim3((unsigned)g.num_tiles),
                        dim3(WAVES * kWave), lds_bytes, stream, op, g, static_cast<uint8_t*>(ws));
     return RLSCAN_OK;
 }

@@ -12,8 +12,8 @@ sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 import bench  # noqa: E402
 
 COPY = "__amd_rocclr_copyBuffer"
-GAE = "void rlscan::scan_kernel<rlscan::GaeOp<3u, false>, 8, 2, false>(rlscan::GaeOp<3u, false>, rlscan::Geo, unsigned char*)"
-VTR = "void rlscan::scan_kernel<rlscan::VtraceOp<16u, false>, 8, 2, false>(rlscan::VtraceOp<16u, false>, rlscan::Geo, unsigned char*)"
+GAE = "void rlscan::scan_kernel<rlscan::GaeOp<3u, false>, 8, 2, false, true>(rlscan::GaeOp<3u, false>, rlscan::Geo, unsigned char*)"
+VTR = "void rlscan::scan_kernel<rlscan::VtraceOp<16u, false>, 8, 2, false, true>(rlscan::VtraceOp<16u, false>, rlscan::Geo, unsigned char*)"
 
 
 def _write_counters(d, counter, rows):
@@ -63,7 +63,7 @@ def test_summary_picks_the_calibration_copy_by_size(tmp_path):
     assert f"source_hash: {bench.source_hash()}" in traffic
     # the per-workload table holds both kernels, each scaled by the same factors
     assert "| gae_truncations_4096x1024 |" in text
-    assert "| vtrace_1024x4096 | `scan_kernel<VtraceOp<16u, false>, 8, 2, false>` | 67108864 | 33554432 |" in text
+    assert "| vtrace_1024x4096 | `scan_kernel<VtraceOp<16u, false>, 8, 2, false, true>` | 67108864 | 33554432 |" in text
 
 
 def test_summary_without_a_calibration_copy_writes_no_traffic(tmp_path):
@@ -101,5 +101,5 @@ def test_summary_tabulates_the_sq_counter_pass(tmp_path):
     text = (out / "scan_kernels_bench_default_kernel_trace.md").read_text()
     assert "## SQ counters" in text
     # 2,220,032 VALU instructions over 8192 waves = 271 per wave; median VALU busy 12.0
-    assert "| `scan_kernel<GaeOp<3u, false>, 8, 2, false>` | 3 | 271 | 12.0 | 45.0 | 0.50 |" in text
+    assert "| `scan_kernel<GaeOp<3u, false>, 8, 2, false, true>` | 3 | 271 | 12.0 | 45.0 | 0.50 |" in text
     assert "copyBuffer" not in text.split("## SQ counters")[1]
