@@ -193,6 +193,7 @@ constexpr int64_t kNormMaxThreadsTotal = 256 * 1024;  // workgroups x threads at
 // element k * THREADS + thread for k < 16.
 template <int THREADS, bool VEC>
 struct NormChunk {
+    static constexpr int64_t kChunkMax = (int64_t)THREADS * kNormVecs * 4;
     float v[kNormVecs * 4];
 
     __device__ __forceinline__ int64_t index(int64_t base, int k, int c) const {
@@ -231,7 +232,11 @@ struct NormChunk {
                 x.y = (v[4 * k + 1] - mean) * inv;
                 x.z = (v[4 * k + 2] - mean) * inv;
                 x.w = (v[4 * k + 3] - mean) * inv;
-                *reinterpret_cast<f32x4*>(adv + i) = x;
+                // with device scope, over the chunk (see store16): 27.9-28.0 ->
+                // 26.5-26.9 us per normalised 4096 x 1024 call
+                const int64_t left = n - base;
+                const uint32_t extent = (uint32_t)(left < kChunkMax ? left : kChunkMax) * 4u;
+                store16<true>(adv + base, (uint32_t)(i - base) * 4u, extent, x);
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
