@@ -62,13 +62,23 @@ __device__ __forceinline__ void load_u8_group(const uint8_t* __restrict__ tp, co
     }
 }
 
-template <bool BACKWARD, bool FAST>
+// SC1: the 8-byte store is a raw buffer store over the tile with device scope
+// (see store16).  On the compact streaming pattern (3 bf16 + 2 byte-flag
+// inputs, 2 bf16 outputs, 4 per lane) it took 9.16-9.19 us against 9.56-9.60
+// for the plain store; pairing lanes into 16-byte stores took 9.43-9.47.
+template <bool BACKWARD, bool FAST, bool SC1 = false>
 __device__ __forceinline__ void store_bf16_group(__bf16* __restrict__ tp, const Grp& gr,
                                                  const float (&in)[4]) {
     if constexpr (FAST) {
         u32x2 v;
         v.x = pack_bf16(in[BACKWARD ? 3 : 0], in[BACKWARD ? 2 : 1]);
         v.y = pack_bf16(in[BACKWARD ? 1 : 2], in[BACKWARD ? 0 : 3]);
+        if constexpr (SC1 && RLSCAN_SC1_STORES) {
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+                tp, (short)0, (int)((gr.last + 1u) * 2u), kRawBufferWord3);
+            __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)(gr.off * 2u), 0, kCachePolicySc1);
+            return;
+        }
         *reinterpret_cast<u32x2*>(const_cast<__bf16*>(&tile_elem<__bf16>(tp, gr.off))) = v;
     } else {
 #pragma unroll

@@ -18,6 +18,7 @@ struct GaeCompactOp {
     static constexpr bool kEdgesAtLoad = (F & kTrunc) == 0;
     static constexpr bool kFits64 = true;
     GaeCompactArgs p;
+    __host__ __device__ int output_arrays() const { return p.returns ? 2 : 1; }
     struct Raw {
         float R[G], V[G], TE[G], TR[G], B[G];
         float halo;
@@ -78,15 +79,15 @@ struct GaeCompactOp {
         }
     }
 
-    template <bool FAST>
+    template <bool FAST, bool SC1 = false>
     __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
                              const float (&)[G], const float (&)[G], const Keep (&kp)[G]) const {
-        store_bf16_group<true, FAST>(reinterpret_cast<__bf16*>(p.advantages) + tl.lo, gr, A);
+        store_bf16_group<true, FAST, SC1>(reinterpret_cast<__bf16*>(p.advantages) + tl.lo, gr, A);
         if (p.returns) {
             float R[G];
 #pragma unroll
             for (int j = 0; j < G; ++j) R[j] = A[j] + kp[j].v;
-            store_bf16_group<true, FAST>(reinterpret_cast<__bf16*>(p.returns) + tl.lo, gr, R);
+            store_bf16_group<true, FAST, SC1>(reinterpret_cast<__bf16*>(p.returns) + tl.lo, gr, R);
         }
     }
 };
