@@ -58,7 +58,8 @@ rlscan_status rlscan_debug_set_lookback_jitter(uint32_t seed);
  * writes num_outputs fp32 arrays of n elements each (outputs[o][i] = the sum
  * of inputs[.][i]), with the access pattern and launch shape of the scan
  * kernels (512-thread workgroups over 4096-element tiles, 16-byte
- * non-temporal loads all issued before any store) and no scan.  Its duration
+ * non-temporal loads all issued before any store, 16-byte stores with device
+ * scope, the faster of the scans' two store forms) and no scan.  Its duration
  * is what the memory system delivers to that pattern; a scan kernel moving
  * the same arrays can be compared with it.  (num_inputs, num_outputs) is one
  * of (1,1), (2,1), (3,1), (4,1), (4,2), (5,2), (6,2).  `inputs` and `outputs`
