@@ -54,7 +54,7 @@ struct GaeOp {
                 load_group<G, true, FAST>(p.bootstrap_values + tl.lo, gr, w.B);
         }
         if constexpr ((F & kSkip) != 0) load_group<G, true, FAST>(p.skip + tl.lo, gr, w.SK);
-        w.halo = (lane_id() == 0 && si.halo_valid) ? p.values[si.halo_flat] : 0.f;
+        w.halo = (lane_id() == 0 && si.halo_valid) ? load_halo_elem(p.values + si.halo_flat) : 0.f;
     }
 
     // Without truncations: the continuation value of a row end in the group.

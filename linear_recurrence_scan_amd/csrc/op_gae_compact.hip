@@ -49,7 +49,7 @@ struct GaeCompactOp {
         // of the array, a row end, and does not use it)
         const int64_t h = si.halo_valid ? si.halo_flat : tl.lo;
         const float keep = (lane_id() == 0 && si.halo_valid) ? 1.f : 0.f;
-        w.halo = (float)bf(p.values)[h] * keep;
+        w.halo = (float)load_halo_elem(bf(p.values) + h) * keep;
     }
 
     // Without truncations: the continuation value of a row end in the group.

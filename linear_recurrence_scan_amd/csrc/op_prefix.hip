@@ -28,7 +28,7 @@ struct PrefixOp {
                          Raw& w) const {
         load_group<G, false, FAST>(p.inputs + tl.lo, gr, w.X);
         load_group<G, false, FAST>(p.dones + tl.lo, gr, w.D);
-        w.halo = (!p.starts_at && lane_id() == 0 && si.halo_valid) ? p.dones[si.halo_flat] : 0.f;
+        w.halo = (!p.starts_at && lane_id() == 0 && si.halo_valid) ? load_halo_elem(p.dones + si.halo_flat) : 0.f;
     }
 
     // The seed of each row that starts in the group.

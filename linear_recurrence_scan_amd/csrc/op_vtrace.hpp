@@ -66,7 +66,7 @@ struct VtraceOp {
         if constexpr ((F & kTrunc) != 0) load_group<G, true, FAST>(p.truncateds + tl.lo, gr, w.TR);
         if constexpr ((F & kBoot2D) != 0)
             load_group<G, true, FAST>(p.bootstrap_values + tl.lo, gr, w.B);
-        w.halo = (lane_id() == 0 && si.halo_valid) ? p.values[si.halo_flat] : 0.f;
+        w.halo = (lane_id() == 0 && si.halo_valid) ? load_halo_elem(p.values + si.halo_flat) : 0.f;
     }
 
     // Without the full bootstrap array: the continuation value of a row end.
