@@ -209,6 +209,19 @@ rlscan_status rlscan_gae_noalloc(const float* rewards, const float* values,
  * workspace of rlscan_gae_norm_workspace_bytes(E, T) bytes is required at
  * every shape (zeroed once with rlscan_workspace_init; it serves the other
  * entry points of the stream too).
+ * Launches.  When every workgroup of the planned scan fits on the device at
+ * once (about 4M steps at most on MI355X) and rows have at least 4 steps,
+ * the call is ONE kernel: each workgroup parks its advantages on chip while
+ * the batch statistics are merged across the workgroups, then writes them
+ * normalised (28 bytes per step moved with returns, as rlscan_gae).  That
+ * kernel's workgroups wait for one another, so it relies on all of them
+ * becoming resident: kernels of other streams that hold compute units only
+ * delay it until their own workgroups exit, but a wait that lasts about a
+ * second gives up, the advantages are then NaN and the workspace's error
+ * word is set (rlscan_workspace_error).  Other batches take two kernels:
+ * the scan with per-tile statistics, then a normalising pass over the
+ * advantages (36 bytes per step).  Both forms give the same values up to
+ * rounding order.
  * Errors  as rlscan_gae; eps < 0 or NaN -> BAD_PARAM; missing, misaligned or
  *         small workspace -> WORKSPACE.
  */

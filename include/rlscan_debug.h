@@ -78,7 +78,15 @@ rlscan_status rlscan_debug_stream(const float* const* inputs, int num_inputs,
  * constant clock at six phases to stamps[8q + k]: k = 0 tile start, 1 loads
  * issued, 2 the first wave's segments loaded and scanned, 3 the workgroup's
  * total known, 4 the carry into the tile known (after the look-back), 5 the
- * outputs' stores issued; entries 6 and 7 are left alone.  `stamps` is a
+ * outputs' stores issued (for rlscan_gae_norm in one kernel: the advantages
+ * parked on chip, before the tile's statistics are published and the
+ * returns stored); the one-kernel rlscan_gae_norm also writes 6 the batch
+ * statistics known and 7 the normalised advantages' stores issued, and
+ * every other launch leaves entries 6 and 7 alone.  In that kernel the tile
+ * that merges the statistics (the last block) also writes, past the tiles'
+ * entries, stamps[8 * tiles] when it has seen every tile's statistics and
+ * stamps[8 * tiles + 1] when it has published the result, if max_tiles is
+ * larger than the tile count.  `stamps` is a
  * DEVICE array of 8 * max_tiles uint64 (8-byte aligned); NULL turns stamping
  * off.  Other builds return BAD_PARAM for a non-NULL buffer and report 0 from
  * rlscan_debug_phase_stamps_built.  Process-wide; set it while no other
@@ -107,6 +115,24 @@ rlscan_status rlscan_debug_set_lookback_polls(int mode);
  * still exits normally.  Process-wide; set it while no other thread is
  * calling the library.  Always returns RLSCAN_OK. */
 rlscan_status rlscan_debug_set_spin_limit(uint32_t polls);
+
+/* How rlscan_gae_norm is launched, for every later call in the process:
+ * 0 (the default) one kernel when the batch fits the device in one round of
+ * workgroups, else two; 1 always the two kernels (scan with per-tile
+ * statistics, then the normalising pass).  The switch exists to compare the
+ * two forms.  Process-wide; set it while no other thread is calling the
+ * library.  Errors: any other mode -> BAD_PARAM. */
+rlscan_status rlscan_debug_set_norm_launches(int mode);
+
+/* Whether rlscan_gae_norm over num_envs x seq_len steps, with truncateds
+ * given (nonzero `truncateds`) and a full [E,T] bootstrap array (nonzero
+ * `bootstrap_2d`, only with truncateds), takes the single kernel on the
+ * current device under the current settings: *single = 1, else 0.  Reads
+ * the device's occupancy (cached); enqueues nothing.
+ * Errors: NULL single -> NULL_ARG; num_envs or seq_len < 1, or too large ->
+ * BAD_SHAPE; bootstrap_2d without truncateds -> CONFLICT. */
+rlscan_status rlscan_debug_norm_single_launch(int64_t num_envs, int64_t seq_len, int truncateds,
+                                              int bootstrap_2d, int* single);
 
 #ifdef __cplusplus
 }

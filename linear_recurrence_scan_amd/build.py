@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librlscan.so")
 # The same library with per-tile phase stamps compiled in (profiling only).
 STAMPS_LIB = os.path.join(HERE, "librlscan_stamps.so")
-HIP_SOURCES = ["op_gae.hip", "op_gae_skip.hip", "op_gae_compact.hip", "op_gae_norm.hip", "op_vtrace.hip", "op_vtrace_clip.hip", "op_returns.hip",
+HIP_SOURCES = ["op_gae.hip", "op_gae_skip.hip", "op_gae_compact.hip", "op_gae_norm.hip", "op_gae_norm_one.hip", "op_vtrace.hip", "op_vtrace_clip.hip", "op_returns.hip",
                "op_prefix.hip", "op_retrace.hip", "op_traces_vec.hip", "aux_kernels.hip",
                "noalloc.hip"]
 HOST_SOURCES = ["rlscan_api.cpp"]

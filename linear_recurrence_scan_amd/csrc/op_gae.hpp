@@ -24,10 +24,18 @@ struct GaeOp {
     static constexpr int G = 4;
     static constexpr bool BACKWARD = true;
     static constexpr bool kEdgesAtLoad = (F & kTrunc) == 0;
-    static constexpr bool kStats = (F & kStatsOut) != 0;
+    // kNormOne: the advantages are held until the batch statistics are
+    // merged inside the launch, then written normalised (one round only);
+    // the epilogue then writes the returns only, from A and Keep.
+    static constexpr bool kHold = (F & kNormOne) != 0;
+    static constexpr bool kStats = (F & (kStatsOut | kNormOne)) != 0;
     static constexpr bool kFits64 = !kStats;
     GaeArgs p;
     __device__ double* stats_out() const { return p.tile_stats; }
+    __device__ float* held_out() const { return p.advantages; }
+    __device__ uint64_t* norm_words() const { return p.norm_words; }
+    __device__ float norm_eps() const { return p.eps; }
+    __device__ double* norm_user() const { return p.user_stats; }
     __host__ __device__ int output_arrays() const { return p.returns ? 2 : 1; }
     struct Raw {
         float R[G], V[G], TE[G], TR[G], B[G];  // B: full bootstrap array (kBoot2D)
@@ -96,7 +104,7 @@ struct GaeOp {
     template <bool FAST, bool SC1 = false>
     __device__ void epilogue(const Tile& tl, const Grp& gr, const float (&A)[G], const float (&)[G],
                              const float (&)[G], const float (&)[G], const Keep (&kp)[G]) const {
-        store_group<G, true, FAST, SC1>(p.advantages + tl.lo, gr, A);
+        if constexpr (!kHold) store_group<G, true, FAST, SC1>(p.advantages + tl.lo, gr, A);
         if (p.returns) {
             float R[G];
 #pragma unroll

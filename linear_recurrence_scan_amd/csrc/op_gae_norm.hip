@@ -2,7 +2,8 @@
 // plans fused advantage normalisation; the formula is the usual whitening of
 // PPO advantages):
 //   adv_t = (A_t - mean) / (std + eps),  mean and unbiased std over all E*T steps.
-// Two launches on the stream:
+// Batches whose tiles are all resident at once take a single launch instead
+// (op_gae_norm_one.hip).  Otherwise two launches on the stream:
 //   1. the GAE scan, whose tiles also reduce their advantages to a
 //      (count, mean, M2) triple in the workspace (scan_tile's statistics);
 //   2. an elementwise pass that normalises the advantages in place.  Each of
@@ -323,12 +324,21 @@ rlscan_status launch_fused(float* adv, int64_t N, const double* tiles, int64_t n
 }  // namespace
 
 rlscan_status launch_gae_norm(const GaeArgs& args, const Plan& plan, void* ws, size_t stats_off,
-                              int64_t N, float eps, double* stats_out, hipStream_t s) {
+                              size_t words_off, bool single_ok, int64_t N, float eps,
+                              double* stats_out, hipStream_t s) {
     GaeArgs a = args;
+    rlscan_status st;
+    if (single_ok) {
+        a.norm_words = reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(ws) + words_off);
+        a.eps = eps;
+        a.user_stats = stats_out;
+        bool launched = false;
+        st = launch_gae_norm_one(a, plan, ws, s, launched);
+        if (st != RLSCAN_OK || launched) return st;
+    }
     double* tiles = reinterpret_cast<double*>(static_cast<uint8_t*>(ws) + stats_off);
     double* result = tiles + 4 * plan.geo.num_tiles;
     a.tile_stats = tiles;
-    rlscan_status st;
     if (!a.truncateds)
         st = launch_gae_op<kStatsOut>(a, plan, ws, s);
     else if (!a.bootstrap_values)

@@ -28,6 +28,7 @@ bool known_shape(int t, int w) {
 std::atomic<uint32_t> g_jitter{0};  // look-back stress delay seed (0 = off)
 std::atomic<uint32_t> g_spins{kSpinLimit};  // polls before a look-back wait gives up
 std::atomic<int> g_device_polls{0};  // 1: look-back polls through the device-scope window only
+std::atomic<int> g_norm_launches{0};  // 1: normalisation always in two launches
 std::atomic<uint64_t*> g_stamps{nullptr};    // phase-stamp buffer (profiling builds)
 std::atomic<int64_t> g_stamp_tiles{0};
 std::atomic<int> g_shape{-1};  // tile << 4 | waves; -1 = not read from the environment yet
@@ -259,6 +260,15 @@ size_t norm_stats_offset(int64_t E, int64_t T) {
     return ((size_t)WsHeader::kSlotsByteOffset + (size_t)tiles * 32u + 255u) & ~(size_t)255u;
 }
 
+// Byte offset of the tagged words of the single-launch normalisation: past
+// the per-tile statistics (32 bytes per tile and 64 more), 256-byte aligned.
+// The two regions never share bytes, so a word of either form is never read
+// as the other.
+size_t norm_words_offset(int64_t E, int64_t T) {
+    const int64_t tiles = (E * T + kMinTile - 1) / kMinTile;
+    return (norm_stats_offset(E, T) + (size_t)tiles * 32u + 64u + 255u) & ~(size_t)255u;
+}
+
 // Look-back words of one vector-trace tile: 3 per column, 64 lanes of up to 4
 // columns each (sized for 4 whatever the launch uses).
 constexpr size_t kVecWordsPerTile = 3 * 4 * 64;
@@ -364,7 +374,7 @@ size_t rlscan_workspace_bytes(int64_t num_envs, int64_t seq_len) {
 size_t rlscan_gae_norm_workspace_bytes(int64_t num_envs, int64_t seq_len) {
     if (check_shape(num_envs, seq_len) != RLSCAN_OK || empty_batch(num_envs, seq_len)) return 0;
     const int64_t tiles = (num_envs * seq_len + kMinTile - 1) / kMinTile;
-    return norm_stats_offset(num_envs, seq_len) + (size_t)tiles * 32u + 64u;
+    return norm_words_offset(num_envs, seq_len) + 8u * (size_t)kNormTileWord0 + (size_t)tiles * 32u;
 }
 
 rlscan_status rlscan_gae_norm(const float* rewards, const float* values, const float* terminateds,
@@ -397,7 +407,9 @@ rlscan_status rlscan_gae_norm(const float* rewards, const float* values, const f
     RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, vec, true));
     GaeArgs a{rewards, values, terminateds, truncateds, bootstrap_values, last_value,
               advantages, returns, gamma, lambda, nullptr, nullptr};
-    return launch_gae_norm(a, plan, ws, norm_stats_offset(num_envs, seq_len), num_envs * seq_len,
+    return launch_gae_norm(a, plan, ws, norm_stats_offset(num_envs, seq_len),
+                           norm_words_offset(num_envs, seq_len),
+                           g_norm_launches.load(std::memory_order_relaxed) == 0, num_envs * seq_len,
                            eps, stats, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -703,6 +715,31 @@ rlscan_status rlscan_debug_set_phase_stamps(uint64_t* stamps, int64_t max_tiles)
 rlscan_status rlscan_debug_set_lookback_polls(int mode) {
     if (mode != 0 && mode != 1) return set_error(RLSCAN_ERR_BAD_PARAM, "lookback poll mode must be 0 or 1");
     g_device_polls.store(mode, std::memory_order_relaxed);
+    return RLSCAN_OK;
+}
+
+rlscan_status rlscan_debug_set_norm_launches(int mode) {
+    if (mode != 0 && mode != 1) return set_error(RLSCAN_ERR_BAD_PARAM, "normalisation launch mode must be 0 or 1");
+    g_norm_launches.store(mode, std::memory_order_relaxed);
+    return RLSCAN_OK;
+}
+
+rlscan_status rlscan_debug_norm_single_launch(int64_t num_envs, int64_t seq_len, int truncateds,
+                                              int bootstrap_2d, int* single) {
+    if (!single) return set_error(RLSCAN_ERR_NULL_ARG, "single must not be NULL");
+    *single = 0;
+    RLSCAN_TRY(check_shape(num_envs, seq_len));
+    if (num_envs < 1 || seq_len < 1) return set_error(RLSCAN_ERR_BAD_SHAPE, "num_envs and seq_len must be >= 1");
+    if (bootstrap_2d && !truncateds)
+        return set_error(RLSCAN_ERR_CONFLICT, "a full bootstrap array is read only with truncateds");
+    Plan plan;
+    RLSCAN_TRY(plan_g4(num_envs, seq_len, plan, true, true));
+    // only which streams are present matters here, not where they are
+    static const float dummy = 0.f;
+    GaeArgs a{};
+    a.truncateds = truncateds ? &dummy : nullptr;
+    a.bootstrap_values = bootstrap_2d ? &dummy : nullptr;
+    *single = (g_norm_launches.load(std::memory_order_relaxed) == 0 && gae_norm_one_fits(a, plan)) ? 1 : 0;
     return RLSCAN_OK;
 }
 

@@ -18,7 +18,18 @@ struct GaeArgs {
     float gamma, lambda;
     const float* skip;  // observation-skip mask, or null
     double* tile_stats; // per-tile (count, mean, M2) of the advantages, or null
+    // Normalisation inside the scan's own launch (kNormOne): the tagged words
+    // of the grid-wide statistics, eps, and where the mean and std go (or null).
+    uint64_t* norm_words;
+    double* user_stats;
+    float eps;
 };
+// norm_words: kNormCopies copies of the result, kNormCopyWords words apart,
+// then tile q's statistics from word kNormTileWord0 + 4q (scan_kernel.hpp,
+// kHold ops).
+constexpr int kNormCopies = 64;
+constexpr int kNormCopyWords = 32;
+constexpr int kNormTileWord0 = kNormCopies * kNormCopyWords;
 
 // Compact rollout format: bf16 values (raw 16-bit storage), one-byte flags.
 struct GaeCompactArgs {
@@ -99,8 +110,19 @@ rlscan_status launch_gae(const GaeArgs& a, const Plan& plan, void* ws, hipStream
 rlscan_status launch_gae_skip(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s);
 // GAE writing per-tile statistics, then the batch statistics and the
 // normalisation of the advantages in place (op_gae_norm.hip).
+// With `single_ok`, a batch whose tiles are all resident at once takes one
+// launch instead (op_gae_norm_one.hip), using the words at `words_off`.
 rlscan_status launch_gae_norm(const GaeArgs& a, const Plan& plan, void* ws, size_t stats_off,
-                              int64_t N, float eps, double* stats_out, hipStream_t s);
+                              size_t words_off, bool single_ok, int64_t N, float eps,
+                              double* stats_out, hipStream_t s);
+// The single-launch normalisation: launched = false (and nothing enqueued)
+// when the planned grid does not fit one round or the rows are shorter than
+// four steps.  `a` carries norm_words, eps and user_stats.
+rlscan_status launch_gae_norm_one(const GaeArgs& a, const Plan& plan, void* ws, hipStream_t s,
+                                  bool& launched);
+// Whether launch_gae_norm_one would launch this plan (reads the device's
+// occupancy, cached; enqueues nothing).
+bool gae_norm_one_fits(const GaeArgs& a, const Plan& plan);
 rlscan_status launch_gae_compact(const GaeCompactArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_vtrace(const VtraceArgs& a, const Plan& plan, void* ws, hipStream_t s);
 rlscan_status launch_retrace(const RetraceArgs& a, const Plan& plan, void* ws, hipStream_t s);

@@ -41,11 +41,23 @@ namespace rlscan {
 // Phase stamps (profiling builds, RLSCAN_PHASE_STAMPS): thread 0 of tile q
 // writes the 100 MHz constant clock to stamps[8q + k] at phase k: 0 entry,
 // 1 loads issued, 2 first segment's data in and scanned, 3 workgroup total
-// known, 4 carry known, 5 stores issued.  Other builds compile it away.
+// known, 4 carry known, 5 stores issued (kHold ops: outputs parked in LDS);
+// normalising launches (kHold ops) also 6 batch statistics known, 7
+// normalised stores issued.  Other builds compile it away.
 __device__ __forceinline__ void stamp(const Geo& g, int64_t q, int k) {
 #ifdef RLSCAN_PHASE_STAMPS
     if (g.stamps && threadIdx.x == 0 && q < g.stamp_tiles)
         g.stamps[8 * q + k] = __builtin_amdgcn_s_memrealtime();
+#endif
+}
+
+// Phase stamps past the tiles' own (profiling builds): stamps[8 * num_tiles
+// + k], written by thread 0 of the tile that merges a normalising launch's
+// statistics: k = 0 every tile's statistics seen, 1 the result published.
+__device__ __forceinline__ void stamp_extra(const Geo& g, int64_t num_tiles, int k) {
+#ifdef RLSCAN_PHASE_STAMPS
+    if (g.stamps && threadIdx.x == 0 && num_tiles < g.stamp_tiles)
+        g.stamps[8 * num_tiles + k] = __builtin_amdgcn_s_memrealtime();
 #endif
 }
 
@@ -59,6 +71,7 @@ enum : unsigned {
     kSameClip = 16u,     // V-trace rho_bar == c_bar
     kSkip = 32u,         // GAE observation-skip mask given
     kStatsOut = 64u,     // per-tile statistics of the outputs written (advantage normalisation)
+    kNormOne = 128u,     // advantages normalised over the batch inside the same launch
 };
 
 struct SegInfo {
@@ -148,6 +161,221 @@ struct WantsStats<Op, std::void_t<decltype(Op::kStats)>> {
     static constexpr bool value = Op::kStats;
 };
 
+// Ops that declare `static constexpr bool kHold = true` keep their first
+// output in registers until statistics over the whole launch are known, then
+// write it normalised: out = (y - mean) / (std + eps), mean and unbiased std
+// over every output of the batch (whitening of PPO advantages; the
+// rl-triton paper, Sec. 9.3, plans the normalisation fused into the scan).
+// Such a launch must have every workgroup resident at once (one round); the
+// host only launches it then.  The op supplies held_out() (the array),
+// norm_words(), norm_eps() and norm_user() (mean and std as two doubles, or
+// null).
+template <class Op, class = void>
+struct HoldsOutput {
+    static constexpr bool value = false;
+};
+template <class Op>
+struct HoldsOutput<Op, std::void_t<decltype(Op::kHold)>> {
+    static constexpr bool value = Op::kHold;
+};
+
+// The grid-wide statistics of a kHold launch, in the 64-bit tagged words of
+// the op's norm_words() (each word: tag << 32 | 32 value bits, written and
+// read as single-copy atomic 64-bit accesses, so a word with the current tag
+// carries its own value; tag = 2 * epoch + 2 of the call, so words of earlier
+// calls never match):
+//   words[32c .. 32c + 3]  copy c < 64 of the result: mean (low, high half),
+//                          std (low, high half); tile q polls copy q mod 64,
+//                          256 bytes apart, so 1024 polling tiles do not
+//                          all queue on one address
+//   words[kNormTileWord0 + 4q ...]  tile q's (count, mean, M2) as floats
+// Every tile publishes its triple.  The launch's last tile (dispatched
+// last, so the likeliest to finish its own scan last) then waits for all of
+// them, merges them in a fixed order in double precision and publishes the
+// result; every tile waits for the result.  No fence and no counter: each
+// word validates itself.  Every wait is bounded (the look-back's spin limit): a wait that
+// gives up sets the workspace's error word and takes NaN statistics, so the
+// failure shows in the outputs.
+struct NormShared {
+    double part[8][3];  // per-wave sums of the merge (the merging tile)
+    float mean, inv;
+    uint32_t tag;
+};
+
+__device__ __forceinline__ void norm_publish_tile(uint64_t* words, int64_t q, uint32_t tag,
+                                                  float n, float m, float m2) {
+    uint64_t* p = words + kNormTileWord0 + 4 * q;
+    slot_store(p + 0, tag, n);
+    slot_store(p + 1, tag, m);
+    slot_store(p + 2, tag, m2);
+}
+
+__device__ __forceinline__ void publish_double(uint64_t* p, uint32_t tag, double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    slot_store(p + 0, tag, __uint_as_float((uint32_t)u));
+    slot_store(p + 1, tag, __uint_as_float((uint32_t)(u >> 32)));
+}
+
+// Sum over the 64 lanes of a wave in double precision, in a fixed order
+// (the same bits on every call): within each row of 16 lanes, neighbour and
+// pair swaps (quad permutations) and rotations by 4 and 8 lanes leave the
+// row's sum in its lane 0; the four row sums are added in row order.  Every
+// lane receives the total.
+template <int CTRL>
+__device__ __forceinline__ double dpp_move_f64(double x) {
+    const long long u = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)u, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+__device__ __forceinline__ double lane_f64(double x, int lane) {
+    const long long u = __double_as_longlong(x);
+    const int lo = __builtin_amdgcn_readlane((int)u, lane);
+    const int hi = __builtin_amdgcn_readlane((int)(u >> 32), lane);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double x) {
+    x += dpp_move_f64<0xB1>(x);   // quad_perm [1,0,3,2]
+    x += dpp_move_f64<0x4E>(x);   // quad_perm [2,3,0,1]
+    x += dpp_move_f64<0x124>(x);  // row_ror:4
+    x += dpp_move_f64<0x128>(x);  // row_ror:8
+    return (lane_f64(x, 0) + lane_f64(x, 16)) + (lane_f64(x, 32) + lane_f64(x, 48));
+}
+
+// Tiles per thread the merge holds (the host launches at most this many
+// tiles per thread of a workgroup in one normalising launch).
+constexpr int kNormTilesPerThread = 4;
+
+// The merging workgroup (the launch's last tile, once its own outputs are
+// parked), every thread: waits until every tile's triple carries this call's
+// tag, then merges them and publishes the batch mean and unbiased std (std 0
+// for a one-element batch).  Thread i holds tiles i + u * THREADS (u < 4).
+// In double precision, with the sums
+//   N = sum n_t,  S1 = sum n_t m_t,  S2 = sum (M2_t + n_t m_t^2),
+//   mean = S1 / N,  M2 = S2 - S1 mean  (= sum of squared deviations),
+// each summed per thread in tile order, over the wave by wave_sum_f64 and
+// over the waves in order: the same bits on every call, and no division
+// until the end.  The subtraction cancels about log10((mean/std)^2) of
+// double's 16 digits, far below the fp32 outputs' precision for any batch
+// whose advantages fit fp32.  num_tiles <= 4 * THREADS.
+template <int WAVES>
+__device__ __forceinline__ void norm_merge(const Geo& g, uint64_t* words, uint32_t num_tiles,
+                                           uint32_t tag, uint32_t spin_limit, uint8_t* ws,
+                                           double* user, NormShared& nsh) {
+    constexpr uint32_t THREADS = WAVES * kWave;
+    constexpr int U = kNormTilesPerThread;
+    const uint64_t* tiles = words + kNormTileWord0;
+    uint64_t w[U][3];
+    bool given_up = false;
+    for (uint32_t spins = 0;; ++spins) {
+        int ok = 1;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {  // every tile's loads in flight at once
+            const uint32_t t = threadIdx.x + u * THREADS;
+            if (t < num_tiles) {
+#pragma unroll
+                for (int k = 0; k < 3; ++k) w[u][k] = slot_load(tiles + 4 * t + k);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (threadIdx.x + u * THREADS < num_tiles &&
+                (tag_of(w[u][0]) != tag || tag_of(w[u][1]) != tag || tag_of(w[u][2]) != tag))
+                ok = 0;
+        if (__syncthreads_and(ok)) break;
+        if (spins >= spin_limit) {
+            given_up = true;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    stamp_extra(g, num_tiles, 0);  // every triple seen
+    double sn = 0.0, s1 = 0.0, s2 = 0.0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (threadIdx.x + u * THREADS >= num_tiles) break;
+        const double n = (double)val_of(w[u][0]), m = (double)val_of(w[u][1]);
+        const double nm = n * m;
+        sn += n;
+        s1 += nm;
+        s2 += fma(nm, m, (double)val_of(w[u][2]));
+    }
+    sn = wave_sum_f64(sn);
+    s1 = wave_sum_f64(s1);
+    s2 = wave_sum_f64(s2);
+    const int wave = (int)(threadIdx.x / kWave);
+    if (lane_id() == 0) {
+        nsh.part[wave][0] = sn;
+        nsh.part[wave][1] = s1;
+        nsh.part[wave][2] = s2;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // every lane of wave 0 forms the same result from the same sums and
+        // publishes its own copy of it
+        double tn = nsh.part[0][0], t1 = nsh.part[0][1], t2 = nsh.part[0][2];
+#pragma unroll
+        for (int v = 1; v < WAVES; ++v) {
+            tn += nsh.part[v][0];
+            t1 += nsh.part[v][1];
+            t2 += nsh.part[v][2];
+        }
+        double mean = t1 / tn;
+        const double m2 = fmax(fma(-t1, mean, t2), 0.0);
+        double sd = tn > 1.0 ? sqrt(m2 / (tn - 1.0)) : 0.0;
+        if (given_up) {
+            if (lane_id() == 0) flag_timeout(ws);
+            mean = sd = __builtin_nan("");
+        }
+        uint64_t* c = words + lane_id() * kNormCopyWords;
+        publish_double(c + 0, tag, mean);
+        publish_double(c + 2, tag, sd);
+        if (user && lane_id() == 0) {
+            user[0] = mean;
+            user[1] = sd;
+        }
+    }
+    stamp_extra(g, num_tiles, 1);  // result published
+}
+
+// One wave, all 64 lanes: waits for the published result (lanes 0-3 read
+// one word each) and returns the mean and 1 / (std + eps) as the floats the
+// outputs are formed with.  A wait that gives up returns NaN.
+__device__ __forceinline__ void norm_wait_result(const uint64_t* words, uint32_t tag,
+                                                 uint32_t spin_limit, uint8_t* ws, float eps,
+                                                 float& mean, float& inv) {
+    const int lane = lane_id();
+    // two polls in flight: the next read is issued before the current one is
+    // examined, so a result that lands between them is seen half a round
+    // trip sooner on average
+    uint64_t next = lane < 4 ? slot_load(words + lane) : 0ull;
+    for (uint32_t spins = 0;; ++spins) {
+        const uint64_t w = next;
+        __builtin_amdgcn_s_sleep(1);
+        next = lane < 4 ? slot_load(words + lane) : 0ull;
+        const bool ok = lane < 4 && tag_of(w) == tag;
+        if ((__ballot(ok) & 0xFull) == 0xFull) {
+            const uint32_t v = (uint32_t)w;
+            const uint64_t m = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)v, 1) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+            const uint64_t s = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)v, 3) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)v, 2);
+            const double md = __longlong_as_double((long long)m);
+            const double sd = __longlong_as_double((long long)s);
+            mean = (float)md;
+            inv = (float)(1.0 / (sd + (double)eps));
+            return;
+        }
+        if (spins >= spin_limit) {
+            if (lane == 0) flag_timeout(ws);
+            mean = inv = __builtin_nanf("");
+            return;
+        }
+    }
+}
+
 // Ops that write their outputs through store_group declare output_arrays()
 // and take the store policy as their epilogue's second template argument;
 // the others store otherwise, and the policy does not apply to them.
@@ -168,7 +396,8 @@ __device__ __forceinline__ void run_epilogue(const Op& op, const Args&... args) 
 template <class Op, int WAVES, int SEGS, bool LOOKBACK, bool FAST, bool SC1>
 __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile& tl, uint8_t* ws,
                                           int64_t q, int64_t stride, uint64_t ticket,
-                                          TileShared& sh, float* lds_wave) {
+                                          TileShared& sh, float* lds_wave, float* held,
+                                          NormShared* norm_shared) {
     constexpr int G = Op::G;
     constexpr bool BACKWARD = Op::BACKWARD;
     constexpr int SEG = kWave * G;
@@ -319,7 +548,17 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
     stamp(g, q, 4);
     // phase 3: apply the carries and write the outputs
     constexpr bool kStats = WantsStats<Op>::value;
+    constexpr bool kHold = HoldsOutput<Op>::value;
+    // A normalising launch without look-back takes its epoch ticket here: its
+    // add completes behind the epilogue, and the returned word is not held
+    // across the tile's loads and scan.
+    if constexpr (kHold && !LOOKBACK)
+        if (threadIdx.x == 0) ticket = epoch_ticket(ws, q);
     Stat st{0.f, 0.f, 0.f};
+    // kHold: the outputs written after the grid-wide merge are parked in the
+    // LDS array `held` (element (s, j) of thread i at [(s*G + j) * threads +
+    // i]: each wave's access is 64 consecutive words), so that no register
+    // stays live across the merge.
     float xs = fmaf(wexcl.b, x, wexcl.a);  // value entering this wave's first segment
 #pragma unroll
     for (int s = 0; s < SEGS; ++s) {
@@ -334,7 +573,14 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
             A[j] = fmaf(be[s][j], y, al[s][j]);
             y = A[j];
         }
-        run_epilogue<FAST, SC1>(op, tl, gr, A, prevA, al[s], be[s], kp[s]);
+        if constexpr (kHold) {
+            // parked; the epilogue (the outputs that need no batch
+            // statistics) runs once the tile's statistics are published
+#pragma unroll
+            for (int j = 0; j < G; ++j) held[(s * G + j) * (WAVES * kWave) + threadIdx.x] = A[j];
+        } else {
+            run_epilogue<FAST, SC1>(op, tl, gr, A, prevA, al[s], be[s], kp[s]);
+        }
         xs = fmaf(segtot[s].b, xs, segtot[s].a);
         if constexpr (kStats) {  // this group's valid outputs, merged into the lane's
             float n = 0.f, sum = 0.f;
@@ -412,22 +658,84 @@ __device__ __forceinline__ void scan_tile(const Op& op, const Geo& g, const Tile
                 }
             }
         }
-        if (threadIdx.x == 0) {
-            double* out = op.stats_out() + 4 * q;
-            out[0] = st.n;
-            out[1] = st.m;
-            out[2] = st.m2;
+        if constexpr (!kHold) {
+            if (threadIdx.x == 0) {
+                double* out = op.stats_out() + 4 * q;
+                out[0] = st.n;
+                out[1] = st.m;
+                out[2] = st.m2;
+            }
         }
+    }
+    if constexpr (kHold) {
+        // The batch statistics, merged across the launch (one round: every
+        // tile is resident), then the held outputs, normalised.
+        NormShared& nsh = *norm_shared;
+        uint64_t* words = op.norm_words();
+        uint32_t tag = 0;
+        if (wave == 0) {
+            // this call's epoch, from the ticket thread 0 took (at tile start
+            // with a look-back, else at the epilogue)
+            uint32_t tlo = (uint32_t)ticket, thi = (uint32_t)(ticket >> 32);
+            asm volatile("" : "+v"(tlo), "+v"(thi));
+            const uint64_t t = readfirstlane_u64(((uint64_t)thi << 32) | tlo);
+            tag = 2u * (uint32_t)(t >> 32) + 2u;
+            if (lane == 0) {
+                if constexpr (!LOOKBACK) epoch_advance(ws, q, g.num_tiles, t);
+                if (g.jitter) jitter_delay(g.jitter ^ 0x2545F491u, q);
+                norm_publish_tile(words, q, tag, st.n, st.m, st.m2);
+            }
+        }
+        // The other outputs (the returns) are stored after the publication,
+        // so their traffic does not delay it; their stores overlap the merge.
+        // The epilogue of a kHold op reads A and its Keep only.
+#pragma unroll
+        for (int s = 0; s < SEGS; ++s) {
+            float A[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) A[j] = held[(s * G + j) * (WAVES * kWave) + threadIdx.x];
+            run_epilogue<FAST, SC1>(op, tl, lane_grp_base(s), A, A, A, A, kp[s]);
+        }
+        if (q == g.num_tiles - 1) {
+            // the last tile merges (q is uniform over the workgroup)
+            if (threadIdx.x == 0) nsh.tag = tag;
+            __syncthreads();
+            norm_merge<WAVES>(g, words, (uint32_t)g.num_tiles, nsh.tag, g.spins, ws, op.norm_user(),
+                              nsh);
+        }
+        if (wave == 0) {
+            float mean, inv;
+            norm_wait_result(words + (q % kNormCopies) * kNormCopyWords, tag, g.spins, ws,
+                             op.norm_eps(), mean, inv);
+            if (lane == 0) {
+                nsh.mean = mean;
+                nsh.inv = inv;
+            }
+            stamp(g, q, 6);
+        }
+        __syncthreads();
+        const float mean = nsh.mean, inv = nsh.inv;
+#pragma unroll
+        for (int s = 0; s < SEGS; ++s) {
+            float o[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+                o[j] = (held[(s * G + j) * (WAVES * kWave) + threadIdx.x] - mean) * inv;
+            store_group<G, BACKWARD, FAST, SC1>(op.held_out() + tl.lo, lane_grp_base(s), o);
+        }
+        stamp(g, q, 7);
     }
 }
 
 // Occupancy the register allocator is held to.  An op whose eight elements
-// per lane fit 64 VGPRs without spilling (Op::kFits64) is held to 8 waves per
-// SIMD in its look-back-free kernels; every other kernel takes what the
-// allocator gives (1 = no constraint).
+// per lane fit 64 VGPRs without spilling (Op::kFits64), and a normalising op
+// (kHold, whose launch must fit one round), are held to 8 waves per SIMD in
+// their look-back-free kernels; every other kernel takes what the allocator
+// gives (1 = no constraint).
 template <class Op, int SEGS, bool LOOKBACK>
 struct WavesPerEu {
-    static constexpr int value = (Op::kFits64 && !LOOKBACK && SEGS * Op::G <= 8) ? 8 : 1;
+    static constexpr int value =
+        (Op::kFits64 || HoldsOutput<Op>::value) && !LOOKBACK && SEGS * Op::G <= 8 ? 8 : 1;
 };
 
 template <class Op, int WAVES, int SEGS, bool LOOKBACK, bool SC1>
@@ -437,12 +745,17 @@ __attribute__((amdgpu_waves_per_eu(WavesPerEu<Op, SEGS, LOOKBACK>::value))) void
     constexpr int TILE = WAVES * SEGS * kWave * Op::G;
     static_assert(WAVES <= 8, "TileShared holds eight waves");
     __shared__ TileShared sh;
+    __shared__ float held[HoldsOutput<Op>::value ? TILE : 1];  // kHold ops only
+    __shared__ std::conditional_t<HoldsOutput<Op>::value, NormShared, char> nsh_storage;
+    NormShared* nsh = nullptr;
+    if constexpr (HoldsOutput<Op>::value) nsh = &nsh_storage;
     extern __shared__ __align__(16) float s_dyn[];
 
     const int64_t q = blockIdx.x;  // tile index in scan order
     stamp(g, q, 0);
     // Every tile of a look-back launch takes its epoch ticket first; the add
-    // completes while the tile's data loads are in flight.
+    // completes while the tile's data loads are in flight.  (A normalising
+    // launch without look-back takes it later, in scan_tile.)
     uint64_t ticket = 0;
     if constexpr (LOOKBACK)
         if (threadIdx.x == 0) ticket = epoch_ticket(ws, q);
@@ -472,9 +785,11 @@ __attribute__((amdgpu_waves_per_eu(WavesPerEu<Op, SEGS, LOOKBACK>::value))) void
     tl.elems = TILE;
     const bool fast = g.vec_ok && rem >= TILE;
     if (fast)
-        scan_tile<Op, WAVES, SEGS, LOOKBACK, true, SC1>(op, g, tl, ws, q, stride, ticket, sh, lds_wave);
+        scan_tile<Op, WAVES, SEGS, LOOKBACK, true, SC1>(op, g, tl, ws, q, stride, ticket, sh, lds_wave,
+                                                         held, nsh);
     else
-        scan_tile<Op, WAVES, SEGS, LOOKBACK, false, SC1>(op, g, tl, ws, q, stride, ticket, sh, lds_wave);
+        scan_tile<Op, WAVES, SEGS, LOOKBACK, false, SC1>(op, g, tl, ws, q, stride, ticket, sh, lds_wave,
+                                                          held, nsh);
 }
 
 // Workgroups of `kernel` (no dynamic LDS) that one device holds at once:
@@ -505,14 +820,15 @@ rlscan_status launch_one(const Op& op, Geo g, void* ws, size_t lds_bytes, hipStr
     const void* k = reinterpret_cast<const void*>(&scan_kernel<Op, WAVES, SEGS, LOOKBACK, false>);
     const int resident = resident_workgroups(k, WAVES * kWave);
     g.boost = (lds_bytes == 0 && g.num_tiles <= resident) ? 1 : 0;
+    const unsigned blocks = (unsigned)g.num_tiles;
     if constexpr (HasOutputArrays<Op>::value) {
         if (sc1_stores(op.output_arrays(), g, resident, LOOKBACK)) {
-            hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, LOOKBACK, true>), dim3((unsigned)g.num_tiles),
+            hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, LOOKBACK, true>), dim3(blocks),
                                dim3(WAVES * kWave), lds_bytes, stream, op, g, static_cast<uint8_t*>(ws));
             return RLSCAN_OK;
         }
     }
-    hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, LOOKBACK, false>), dim3((unsigned)g.num_tiles),
+    hipLaunchKernelGGL((scan_kernel<Op, WAVES, SEGS, LOOKBACK, false>), dim3(blocks),
                        dim3(WAVES * kWave), lds_bytes, stream, op, g, static_cast<uint8_t*>(ws));
     return RLSCAN_OK;
 }

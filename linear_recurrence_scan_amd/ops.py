@@ -103,6 +103,9 @@ def _declare(L):
     L.rlscan_debug_set_lookback_jitter.argtypes = [ctypes.c_uint32]
     L.rlscan_debug_set_spin_limit.argtypes = [ctypes.c_uint32]
     L.rlscan_debug_set_lookback_polls.argtypes = [ctypes.c_int]
+    L.rlscan_debug_set_norm_launches.argtypes = [ctypes.c_int]
+    L.rlscan_debug_norm_single_launch.argtypes = [i64, i64, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.POINTER(ctypes.c_int)]
     L.rlscan_debug_set_phase_stamps.argtypes = [vp, i64]
     L.rlscan_debug_phase_stamps_built.restype = ctypes.c_int
     L.rlscan_debug_stream.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
@@ -114,7 +117,8 @@ def _declare(L):
                  "rlscan_gae_skip", "rlscan_gae_bf16", "rlscan_vtrace", "rlscan_retrace", "rlscan_returns", "rlscan_prefix",
                  "rlscan_check_inputs", "rlscan_debug_set_launch_shape", "rlscan_debug_g4_shape",
                  "rlscan_debug_set_lookback_jitter", "rlscan_debug_set_spin_limit",
-                 "rlscan_debug_set_lookback_polls",
+                 "rlscan_debug_set_lookback_polls", "rlscan_debug_set_norm_launches",
+                 "rlscan_debug_norm_single_launch",
                  "rlscan_debug_stream", "rlscan_debug_set_phase_stamps"):
         getattr(L, name).restype = st
     return L
@@ -411,6 +415,24 @@ def set_lookback_polls(mode=0):
     """0: look-back polls through the XCD's L2 where the layout allows (the
     default); 1: the device-scope window only; see include/rlscan_debug.h."""
     _check("rlscan_debug_set_lookback_polls", lib().rlscan_debug_set_lookback_polls(int(mode)))
+
+
+def set_norm_launches(mode=0):
+    """0: rlscan_gae_norm takes one kernel when the batch fits the device in
+    one round (the default); 1: always the two kernels; see
+    include/rlscan_debug.h."""
+    _check("rlscan_debug_set_norm_launches", lib().rlscan_debug_set_norm_launches(int(mode)))
+
+
+def norm_single_launch(num_envs, seq_len, truncateds=True, bootstrap_2d=True):
+    """Whether rlscan_gae_norm over num_envs x seq_len (with the streams
+    named) takes the single kernel on the current device; see
+    include/rlscan_debug.h."""
+    out = ctypes.c_int(0)
+    _check("rlscan_debug_norm_single_launch",
+           lib().rlscan_debug_norm_single_launch(int(num_envs), int(seq_len), 1 if truncateds else 0,
+                                                 1 if bootstrap_2d else 0, ctypes.byref(out)))
+    return bool(out.value)
 
 
 def set_spin_limit(polls=0):

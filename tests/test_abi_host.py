@@ -288,6 +288,35 @@ def test_lookback_poll_switch_validation(L):
     assert L.rlscan_debug_set_lookback_polls(0) == OK
 
 
+def test_norm_launch_switch_and_query_validation(L):
+    assert L.rlscan_debug_set_norm_launches(2) == BAD_PARAM
+    assert L.rlscan_debug_set_norm_launches(-1) == BAD_PARAM
+    assert L.rlscan_debug_set_norm_launches(1) == OK
+    assert L.rlscan_debug_set_norm_launches(0) == OK
+    out = ctypes.c_int(7)
+    q = L.rlscan_debug_norm_single_launch
+    q.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.POINTER(ctypes.c_int)]
+    assert q(64, 64, 1, 1, None) == NULL_ARG
+    assert q(0, 64, 1, 1, ctypes.byref(out)) == BAD_SHAPE and out.value == 0
+    assert q(64, -1, 1, 1, ctypes.byref(out)) == BAD_SHAPE
+    assert q(64, 1 << 31, 1, 1, ctypes.byref(out)) == BAD_SHAPE
+    assert q(64, 64, 0, 1, ctypes.byref(out)) == CONFLICT
+
+
+def test_norm_workspace_holds_both_regions(L):
+    """The normalisation workspace holds the look-back slots, the per-tile
+    statistics of the two-launch form (32 bytes per 256-step tile, 64 more)
+    and, 256-byte aligned past them, the single launch's tagged words (64
+    copies of the result 256 bytes apart, then 32 bytes per tile)."""
+    for E, T in ((1, 1), (64, 64), (4096, 1024), (3, 4099)):
+        tiles = -(-(E * T) // 256)
+        slots = 4352 + 32 * tiles
+        stats = -(-slots // 256) * 256
+        words = -(-(stats + 32 * tiles + 64) // 256) * 256
+        assert L.rlscan_gae_norm_workspace_bytes(E, T) == words + 64 * 256 + 32 * tiles
+
+
 def test_launch_shape_override_validation(L):
     assert L.rlscan_debug_set_launch_shape(1024, 3) == BAD_PARAM
     assert L.rlscan_debug_set_launch_shape(512, 1) == BAD_PARAM

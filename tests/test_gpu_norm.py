@@ -164,3 +164,114 @@ def test_gae_norm_two_steps_and_constant_advantages():
     r = np.full((E, T), 0.5, f32)
     adv, _, st = ops.gae_normalized(dev(r), dev(z), dev(z), None, 0.0, 0.95)
     assert np.all(host(adv) == 0.0) and host(st)[1] == 0.0
+
+
+# ---- the single-launch form (one kernel when every tile is resident at once) ----
+
+@pytest.fixture
+def restore_switches():
+    yield
+    ops.set_norm_launches(0)
+    ops.set_spin_limit(0)
+    ops.set_lookback_jitter(0)
+
+
+def test_single_launch_is_taken_where_the_batch_fits_one_round(restore_switches):
+    """The 4M-step workload fills the device exactly once (1024 tiles of 4096
+    steps, four 512-thread workgroups per CU): one kernel.  Past one round,
+    and for rows shorter than four steps, two kernels."""
+    assert ops.norm_single_launch(4096, 1024, True, True)
+    assert ops.norm_single_launch(4096, 1024, False, False)
+    assert ops.norm_single_launch(512, 1024, True, True)
+    assert ops.norm_single_launch(37, 1000, True, True)     # rows straddle tiles: look-back too
+    assert not ops.norm_single_launch(8200, 1024, True, True)
+    assert not ops.norm_single_launch(5, 3, False, False)
+    ops.set_norm_launches(1)
+    assert not ops.norm_single_launch(512, 1024, True, True)
+
+
+def normalized(d, eps=1e-8):
+    return ops.gae_normalized(dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]),
+                              dev(d["truncateds"]), 0.99, 0.95, dev(d["bootstrap_values"]),
+                              dev(d["last_value"]), eps=eps, want_returns=True)
+
+
+SINGLE_SHAPES = [
+    (4096, 1024, "2d"),   # the full workload: 1024 tiles of 8 waves x 2 segments
+    (512, 1024, "2d"),    # 512 tiles of 2 waves x 2 segments
+    (1000, 1000, "2d"),   # rows straddle 2048-step tiles of 4 waves: look-back too
+    (37, 1000, "2d"),     # 145 one-wave tiles with look-back
+    (64, 5000, "2d"),     # 4096-step tiles of 4 waves x 4 segments, look-back
+    (200, 257, None),     # no truncations, no bootstrap
+    (64, 515, "last"),    # last_value
+    (1, 20000, "2d"),
+    (2, 100, "last"),     # one partial tile: the merging tile is the only one
+]
+
+
+@pytest.mark.parametrize("E,T,boot", SINGLE_SHAPES)
+def test_single_launch_matches_two_launches(E, T, boot, restore_switches):
+    """Both forms against each other: the returns are the same bits (the same
+    scan), the statistics agree to double rounding (different merge orders),
+    and the normalised advantages to fp32 rounding of mean and 1/(std+eps).
+    Each form is also checked against the oracle (check())."""
+    trunc = boot == "2d"
+    d = synth.gae_inputs(E, T, seed=E * 7 + T, p_term=0.01, p_trunc=0.005 if trunc else 0.0,
+                         truncations=trunc, boot=boot)
+    assert ops.norm_single_launch(E, T, trunc, trunc)
+    a1, s1 = check(d, T, what=f"single {E}x{T}")
+    _, r1, _ = normalized(d)
+    ops.set_norm_launches(1)
+    a2, s2 = check(d, T, what=f"two {E}x{T}")
+    _, r2, _ = normalized(d)
+    assert torch.equal(r1, r2)
+    h1, h2 = host(s1), host(s2)
+    assert np.allclose(h1, h2, rtol=1e-12, atol=1e-300), (h1, h2)
+    g1, g2 = host(a1), host(a2)
+    scale = 1.0 + np.abs(g2) + abs(h2[0]) / (h2[1] + 1e-8)
+    assert np.max(np.abs(g1 - g2) / scale) <= 1e-6
+
+
+def test_single_launch_is_reproducible_under_jitter(restore_switches):
+    """Tiles delayed by a seeded pseudo-random time before they publish their
+    statistics (so they reach the merge in an unrelated order): the same bits
+    as the undelayed call, and on every call."""
+    for E, T in ((512, 1024), (37, 1000)):
+        d = synth.gae_trunc(E=E, T=T, seed=77)
+        a0, _, s0 = normalized(d)
+        a1, _, s1 = normalized(d)
+        for seed in (1, 99, 4242):
+            ops.set_lookback_jitter(seed)
+            aj, _, sj = normalized(d)
+            torch.cuda.synchronize()
+            assert torch.equal(aj, a0) and torch.equal(sj, s0), (E, T, seed)
+        ops.set_lookback_jitter(0)
+        assert torch.equal(a1, a0) and torch.equal(s1, s0)
+    assert ops.workspace_error() == 0
+
+
+def test_single_launch_give_up_is_loud(restore_switches):
+    """Waits held to a one-poll bound, with seeded publication delays: every
+    advantage is NaN or the correct value, NaNs appear exactly when the error
+    word is set, and the returns (stored before the merge) stay exact."""
+    E, T = 512, 1024
+    d = synth.gae_trunc(E=E, T=T, seed=78)
+    want, want_r = None, None
+    a0, r0, _ = normalized(d)
+    want, want_r = host(a0), host(r0)
+    ops.reset_workspace()
+    ops.set_lookback_jitter(31337)
+    ops.set_spin_limit(1)
+    a, r, _ = normalized(d)
+    got, got_r = host(a), host(r)
+    err = ops.workspace_error()
+    nan = np.isnan(got)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert (err != 0) == bool(nan.any()), (err, int(nan.sum()))
+    assert np.array_equal(got_r, want_r)
+    print(f"forced give-ups: error word {err:#x}, {int(nan.sum())} NaN advantages of {got.size}")
+    ops.set_spin_limit(0)
+    ops.set_lookback_jitter(0)
+    ops.reset_workspace()
+    a, _, _ = normalized(d)
+    assert torch.equal(a, a0) and ops.workspace_error() == 0
