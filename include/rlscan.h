@@ -38,6 +38,11 @@
  *   must be zero-filled once before its first use (rlscan_workspace_init);
  *   afterwards each call leaves it ready for the next one, so it needs no
  *   clearing between calls and the calls are safe to record in a HIP graph.
+ *   Each call that uses the workspace advances a 32-bit epoch stored in it,
+ *   and the words it publishes carry that epoch, so words of earlier calls
+ *   never look current -- for 2^31 calls: zero the workspace again with
+ *   rlscan_workspace_init before 2^31 calls have used it (a word left from
+ *   exactly 2^31 calls earlier would carry the current tag).
  *   Calls that share one workspace must be ordered (same stream, or
  *   synchronised); concurrent calls on one workspace race.  Passing NULL /
  *   0 is allowed when the call needs no workspace; when it does,

@@ -58,43 +58,13 @@ __device__ __forceinline__ void load_first_batch(const double* tiles, int64_t nu
         b[u] = load_triple(tiles, threadIdx.x + (int64_t)u * THREADS, num_tiles);
 }
 
-// x from the lane that the DPP control CTRL names, both 32-bit halves moved
-// by the same pattern.
-template <int CTRL>
-__device__ __forceinline__ double dpp_move(double x) {
-    const long long u = __double_as_longlong(x);
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)u, CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(u >> 32), CTRL, 0xF, 0xF, false);
-    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
-
-__device__ __forceinline__ double lane_value(double x, int lane) {
-    const long long u = __double_as_longlong(x);
-    const int lo = __builtin_amdgcn_readlane((int)u, lane);
-    const int hi = __builtin_amdgcn_readlane((int)(u >> 32), lane);
-    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
-
-// Sum over the 64 lanes of a wave, the same value in every lane: within each
-// row of 16 lanes, swaps of neighbours and of pairs (quad permutations) and
-// rotations by 4 and 8 lanes leave the row's sum in its lane 0; the four row
-// sums are then added in row order.  A fixed order: the same bits on every
-// call.
-__device__ __forceinline__ double wave_sum(double x) {
-    x += dpp_move<0xB1>(x);   // quad_perm [1,0,3,2]
-    x += dpp_move<0x4E>(x);   // quad_perm [2,3,0,1]
-    x += dpp_move<0x124>(x);  // row_ror:4
-    x += dpp_move<0x128>(x);  // row_ror:8
-    return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
-}
-
 // Workgroup totals of x[0..K) over its THREADS threads; every thread gets
-// them.  The wave sums (wave_sum) are added in wave order: the same bits on
-// every call.
+// them.  The wave sums (wave_sum_f64, scan_kernel.hpp) are added in wave
+// order: the same bits on every call.
 template <int THREADS, int K>
 __device__ __forceinline__ void block_sum(double (&x)[K], double (&sh)[K][THREADS / 64]) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) x[k] = wave_sum(x[k]);
+    for (int k = 0; k < K; ++k) x[k] = wave_sum_f64(x[k]);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0)
 #pragma unroll

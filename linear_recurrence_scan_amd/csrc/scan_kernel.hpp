@@ -193,9 +193,9 @@ struct HoldsOutput<Op, std::void_t<decltype(Op::kHold)>> {
 // last, so the likeliest to finish its own scan last) then waits for all of
 // them, merges them in a fixed order in double precision and publishes the
 // result; every tile waits for the result.  No fence and no counter: each
-// word validates itself.  Every wait is bounded (the look-back's spin limit): a wait that
-// gives up sets the workspace's error word and takes NaN statistics, so the
-// failure shows in the outputs.
+// word validates itself.  Every wait is bounded (the look-back's spin
+// limit): a wait that gives up sets the workspace's error word and takes NaN
+// statistics, so the failure shows in the outputs.
 struct NormShared {
     double part[8][3];  // per-wave sums of the merge (the merging tile)
     float mean, inv;
