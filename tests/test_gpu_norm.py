@@ -275,3 +275,21 @@ def test_single_launch_give_up_is_loud(restore_switches):
     ops.reset_workspace()
     a, _, _ = normalized(d)
     assert torch.equal(a, a0) and ops.workspace_error() == 0
+
+
+def test_single_launch_many_calls_are_identical(restore_switches):
+    """300 back-to-back one-kernel calls at the full size, 100 of them with
+    seeded publication delays, on one workspace: every call's advantages and
+    statistics are the first call's bits, and no wait gave up."""
+    d = synth.gae_trunc()
+    args = (dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]), dev(d["truncateds"]),
+            0.99, 0.95, dev(d["bootstrap_values"]))
+    a0, _, s0 = ops.gae_normalized(*args)
+    mismatches = 0
+    for i in range(300):
+        ops.set_lookback_jitter(1000 + i if i >= 200 else 0)
+        a, _, s = ops.gae_normalized(*args)
+        mismatches += int(not (torch.equal(a, a0) and torch.equal(s, s0)))
+    torch.cuda.synchronize()
+    assert mismatches == 0
+    assert ops.workspace_error() == 0
