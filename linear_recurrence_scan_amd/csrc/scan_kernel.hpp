@@ -20,7 +20,11 @@
 //                across waves, look-back across workgroups;
 //   3. epilogue: carries applied, outputs written.
 // Nothing is materialised in HBM between those steps (rl-triton paper,
-// Sec. 4.2, Table 2).
+// Sec. 4.2, Table 2).  Ops that normalise an output over the whole batch
+// (kHold, launched only when every tile is resident at once) park that
+// output in LDS in step 3, publish the tile's statistics, write their other
+// outputs, and write the parked one once the launch's last tile has merged
+// every tile's statistics (see HoldsOutput below).
 //
 // Row boundaries are handled by folding the row's boundary carry into alpha
 // and setting beta = 0 at the row's first scan element (paper, Sec. 3.2 and
