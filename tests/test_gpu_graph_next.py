@@ -99,7 +99,7 @@ def test_graph_gae_skip():
         [adv, ret], int(L.rlscan_workspace_bytes(E, T)))
 
 
-@pytest.mark.parametrize("E,T", [(300, 1000), (512, 1024)])
+@pytest.mark.parametrize("E,T", [(300, 1000), (512, 1024), (4096, 1024)])
 def test_graph_gae_norm(E, T):
     L = ops.lib()
     d = synth.gae_trunc(E=E, T=T, seed=44)

@@ -293,3 +293,29 @@ def test_single_launch_many_calls_are_identical(restore_switches):
     torch.cuda.synchronize()
     assert mismatches == 0
     assert ops.workspace_error() == 0
+
+
+def test_single_launch_shares_the_workspace_with_other_calls(restore_switches):
+    """The one-kernel normalisation and the look-back calls share one
+    workspace (its epoch leaves advance once per call of either kind): calls
+    of other entry points between two normalisations leave the second one's
+    bits equal to the first's, and their own results exact."""
+    d = synth.gae_trunc(E=512, T=1024, seed=91)
+    args = (dev(d["rewards"]), dev(d["values"]), dev(d["terminateds"]), dev(d["truncateds"]),
+            0.99, 0.95, dev(d["bootstrap_values"]))
+    a0, _, s0 = ops.gae_normalized(*args)
+    f = synth.forward_inputs(37, 1000, seed=92)       # rows straddle tiles: look-back
+    g = synth.gae_inputs(37, 1000, seed=93, boot="2d")
+    for _ in range(3):
+        p = ops.episodic_prefix_sum(dev(f["inputs"]), dev(f["dones"]))
+        adv = ops.gae(dev(g["rewards"]), dev(g["values"]), dev(g["terminateds"]),
+                      dev(g["truncateds"]), 0.99, 0.95, dev(g["bootstrap_values"]))
+        a1, _, s1 = ops.gae_normalized(*args)
+        torch.cuda.synchronize()
+        assert torch.equal(a1, a0) and torch.equal(s1, s0)
+    want_p = oracle.episodic_prefix_sum(f["inputs"], f["dones"], None, "ends_at")
+    assert np.max(np.abs(host(p) - want_p) / np.maximum(1.0, np.abs(want_p))) <= 1e-4
+    want_a, _ = oracle.gae(g["rewards"], g["values"], g["terminateds"], g["truncateds"], f32(0.99),
+                           f32(0.95), g["bootstrap_values"])
+    assert np.max(np.abs(host(adv) - want_a) / np.maximum(1.0, np.abs(want_a))) <= 1e-4
+    assert ops.workspace_error() == 0
