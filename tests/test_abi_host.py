@@ -392,3 +392,37 @@ def test_python_binding_refuses_cpu_tensors():
         ops.gae(x.double(), x, x)
     with pytest.raises(ValueError, match="boundary"):
         ops._forward(x, x, None, 1.0, "middle")
+
+
+def test_norm_single_launch_indices_stay_in_the_workspace(L):
+    """Host-side replay of every workspace word the one-kernel normalisation
+    forms, for the planner's launch at each shape (on a 256-CU device): tile
+    q's statistics at word 2048 + 4q + k (k < 3, q < tiles), the 64 result
+    copies at words 32c + i (i < 4), all inside the region past the two-kernel
+    form's statistics; and each thread's four merged tiles (i + u * threads,
+    u < 4) cover every tile of a launch the host would take as one kernel.
+    The parked outputs' LDS index (s*4 + j) * threads + i stays below the
+    tile's element count by construction (s < segments, j < 4, i < threads)."""
+    q = L.rlscan_debug_g4_shape
+    q.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                  ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
+    for E, T in ((1, 4), (2, 100), (8, 128), (37, 1000), (64, 515), (200, 257), (512, 1024),
+                 (1000, 1000), (64, 5000), (3, 4099), (1, 20000), (4096, 1024), (4096, 1000),
+                 (2048, 2048), (8200, 1024)):
+        t, w = ctypes.c_int(0), ctypes.c_int(0)
+        assert q(E, T, 0, 256, ctypes.byref(t), ctypes.byref(w)) == OK
+        tile, threads = t.value, 64 * w.value
+        n = E * T
+        tiles = -(-n // tile)
+        tiles_min = -(-n // 256)
+        slots = 4352 + 32 * tiles_min
+        stats = -(-slots // 256) * 256
+        words = -(-(stats + 32 * tiles_min + 64) // 256) * 256
+        total = L.rlscan_gae_norm_workspace_bytes(E, T)
+        last_word = max(63 * 32 + 3, 2048 + 4 * (tiles - 1) + 2)
+        assert words >= stats + 32 * tiles_min + 64   # past the two-kernel statistics
+        assert words + 8 * (last_word + 1) <= total, (E, T, tile, tiles)
+        if tiles <= 4 * threads:                       # a launch the host may take as one kernel
+            merged = {i + u * threads for i in range(threads) for u in range(4)
+                      if i + u * threads < tiles}
+            assert merged == set(range(tiles))
