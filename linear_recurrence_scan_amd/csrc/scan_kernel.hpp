@@ -201,7 +201,7 @@ struct HoldsOutput<Op, std::void_t<decltype(Op::kHold)>> {
 // limit): a wait that gives up sets the workspace's error word and takes NaN
 // statistics, so the failure shows in the outputs.
 struct NormShared {
-    double part[8][3];  // per-wave sums of the merge (the merging tile)
+    double part[8][2];  // per-wave sums of the merge (the merging tile)
     float mean, inv;
     uint32_t tag;
 };
@@ -271,6 +271,10 @@ __device__ __forceinline__ void norm_merge(const Geo& g, uint64_t* words, uint32
     constexpr uint32_t THREADS = WAVES * kWave;
     constexpr int U = kNormTilesPerThread;
     const uint64_t* tiles = words + kNormTileWord0;
+    // The counts add up to N (every step of the batch is counted), so only the
+    // two sums are reduced; the reciprocals are formed before the wait.
+    const double total = (double)g.N;
+    const double r_n = 1.0 / total, r_n1 = total > 1.0 ? 1.0 / (total - 1.0) : 0.0;
     uint64_t w[U][3];
     bool given_up = false;
     for (uint32_t spins = 0;; ++spins) {
@@ -296,39 +300,35 @@ __device__ __forceinline__ void norm_merge(const Geo& g, uint64_t* words, uint32
         __builtin_amdgcn_s_sleep(1);
     }
     stamp_extra(g, num_tiles, 0);  // every triple seen
-    double sn = 0.0, s1 = 0.0, s2 = 0.0;
+    double s1 = 0.0, s2 = 0.0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (threadIdx.x + u * THREADS >= num_tiles) break;
         const double n = (double)val_of(w[u][0]), m = (double)val_of(w[u][1]);
         const double nm = n * m;
-        sn += n;
         s1 += nm;
         s2 += fma(nm, m, (double)val_of(w[u][2]));
     }
-    sn = wave_sum_f64(sn);
     s1 = wave_sum_f64(s1);
     s2 = wave_sum_f64(s2);
     const int wave = (int)(threadIdx.x / kWave);
     if (lane_id() == 0) {
-        nsh.part[wave][0] = sn;
-        nsh.part[wave][1] = s1;
-        nsh.part[wave][2] = s2;
+        nsh.part[wave][0] = s1;
+        nsh.part[wave][1] = s2;
     }
     __syncthreads();
     if (wave == 0) {
         // every lane of wave 0 forms the same result from the same sums and
         // publishes its own copy of it
-        double tn = nsh.part[0][0], t1 = nsh.part[0][1], t2 = nsh.part[0][2];
+        double t1 = nsh.part[0][0], t2 = nsh.part[0][1];
 #pragma unroll
         for (int v = 1; v < WAVES; ++v) {
-            tn += nsh.part[v][0];
-            t1 += nsh.part[v][1];
-            t2 += nsh.part[v][2];
+            t1 += nsh.part[v][0];
+            t2 += nsh.part[v][1];
         }
-        double mean = t1 / tn;
+        double mean = t1 * r_n;
         const double m2 = fmax(fma(-t1, mean, t2), 0.0);
-        double sd = tn > 1.0 ? sqrt(m2 / (tn - 1.0)) : 0.0;
+        double sd = sqrt(m2 * r_n1);
         if (given_up) {
             if (lane_id() == 0) flag_timeout(ws);
             mean = sd = __builtin_nan("");
