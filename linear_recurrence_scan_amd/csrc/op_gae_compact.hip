@@ -17,6 +17,12 @@ struct GaeCompactOp {
     static constexpr bool BACKWARD = true;
     static constexpr bool kEdgesAtLoad = (F & kTrunc) == 0;
     static constexpr bool kFits64 = true;
+    // One-round launches take their tiles in XCD-sized blocks.  Measured on
+    // MI355X, 4096 x 1024, interleaved passes on two boxes: 10.62-10.74 ->
+    // 10.34-10.36 us and 10.50-10.72 -> 10.41-10.67 us (medians 10.58 ->
+    // 10.44).  The fp32 GAE, V-trace and skip-mask kernels lost 0.3-0.8 us
+    // with the same order, so they keep every eighth tile per XCD.
+    static constexpr bool kXcdBlocks = true;
     GaeCompactArgs p;
     __host__ __device__ int output_arrays() const { return p.returns ? 2 : 1; }
     struct Raw {

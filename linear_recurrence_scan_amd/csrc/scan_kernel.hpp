@@ -183,6 +183,19 @@ struct HoldsOutput<Op, std::void_t<decltype(Op::kHold)>> {
     static constexpr bool value = Op::kHold;
 };
 
+// Ops with kXcdBlocks take, in a one-round launch without look-back, their
+// tiles in XCD-sized blocks: MI355X places workgroup i on XCD i mod 8, so
+// tile (i mod 8) * (grid / 8) + i / 8 gives each XCD a contiguous eighth of
+// the tiles instead of every eighth tile.
+template <class Op, class = void>
+struct XcdBlocks {
+    static constexpr bool value = false;
+};
+template <class Op>
+struct XcdBlocks<Op, std::void_t<decltype(Op::kXcdBlocks)>> {
+    static constexpr bool value = Op::kXcdBlocks;
+};
+
 // The grid-wide statistics of a kHold launch, in the 64-bit tagged words of
 // the op's norm_words() (each word: tag << 32 | 32 value bits, written and
 // read as single-copy atomic 64-bit accesses, so a word with the current tag
@@ -755,7 +768,10 @@ __attribute__((amdgpu_waves_per_eu(WavesPerEu<Op, SEGS, LOOKBACK>::value))) void
     if constexpr (HoldsOutput<Op>::value) nsh = &nsh_storage;
     extern __shared__ __align__(16) float s_dyn[];
 
-    const int64_t q = blockIdx.x;  // tile index in scan order
+    int64_t q = blockIdx.x;  // tile index in scan order
+    if constexpr (!LOOKBACK && XcdBlocks<Op>::value)
+        if (g.boost && (gridDim.x & 7u) == 0u)
+            q = (int64_t)(blockIdx.x & 7u) * (int64_t)(gridDim.x >> 3) + (int64_t)(blockIdx.x >> 3);
     stamp(g, q, 0);
     // Every tile of a look-back launch takes its epoch ticket first; the add
     // completes while the tile's data loads are in flight.  (A normalising
